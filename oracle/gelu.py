@@ -1,0 +1,61 @@
+"""bias + GeLU forward and backward, float64 (oracle; test infrastructure only).
+
+Follows the "bias + GeLU" fusion listed under "融合 CUDA 核" on page
+"BLOOM 176B 训练技术概览" (the MLP's GeLU(XA) of section 2.1 on page
+"企业官网建设流程全解析").  The pages do not write GeLU out; the tanh form of
+the GELU paper (Hendrycks and Gimpel, arXiv:1606.08415) is used:
+    u = x + b
+    y = u/2 * (1 + tanh(k (u + c u^3))),   k = sqrt(2/pi), c = 0.044715
+and its derivative, with t = tanh(k (u + c u^3)),
+    y'(u) = (1 + t)/2 + u/2 * (1 - t^2) * k * (1 + 3 c u^2)
+    dx    = dy * y'(u),      dbias = sum over rows of dx (unrounded).
+u = x + b is exact in float64.  Outputs are rounded once to bf16.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .bf16 import round_to_bf16, to_f64
+
+K = math.sqrt(2.0 / math.pi)
+C = 0.044715
+
+
+def gelu(u):
+    return 0.5 * u * (1.0 + np.tanh(K * (u + C * u ** 3)))
+
+
+def gelu_grad(u):
+    t = np.tanh(K * (u + C * u ** 3))
+    return 0.5 * (1.0 + t) + 0.5 * u * (1.0 - t * t) * K * (1.0 + 3.0 * C * u * u)
+
+
+def gelu_grad_terms(u):
+    """Magnitudes of the two terms of gelu_grad, summed."""
+    t = np.tanh(K * (u + C * u ** 3))
+    return np.abs(0.5 * (1.0 + t)) + np.abs(0.5 * u * (1.0 - t * t) * K * (1.0 + 3.0 * C * u * u))
+
+
+def bias_gelu_fwd(x_bits, bias_bits):
+    """y (bf16 bits) for x [rows, cols], bias [cols] (bf16 bits)."""
+    u = to_f64(x_bits) + to_f64(bias_bits)[None, :]
+    return round_to_bf16(gelu(u))
+
+
+def bias_gelu_bwd(dy_bits, x_bits, bias_bits, return_f64: bool = False):
+    """dx and dbias as bf16 bits.
+
+    With ``return_f64`` also returns (dx, dbias, per-element magnitude of dx's
+    terms, column sums of |dx|) in float64.
+    """
+    u = to_f64(x_bits) + to_f64(bias_bits)[None, :]
+    dy = to_f64(dy_bits)
+    dx = dy * gelu_grad(u)
+    dbias = dx.sum(axis=0)
+    out = (round_to_bf16(dx), round_to_bf16(dbias))
+    if not return_f64:
+        return out
+    return out, (dx, dbias, np.abs(dy) * gelu_grad_terms(u), np.abs(dx).sum(axis=0))

@@ -1,0 +1,87 @@
+"""LayerNorm forward and backward, float64 (oracle; test infrastructure only).
+
+Follows the fused LayerNorm kernel listed under "融合 CUDA 核" on page
+"BLOOM 176B 训练技术概览"; the embedding LayerNorm added after the word
+embedding ("架构微调", same page; also section 4.3 of page
+"企业官网建设流程全解析") is the same computation on embedding rows.
+
+The pages name the operation only.  The standard definition is used: per row
+of width H, mean mu = sum(x)/H, biased variance var = sum((x-mu)^2)/H,
+r = 1/sqrt(var + eps) with eps inside the square root, x_hat = (x-mu)*r,
+y = x_hat*gamma + beta.  The backward of that definition is, with
+g = dy*gamma,
+    dx     = r * (g - mean(g) - x_hat * mean(g * x_hat))
+    dgamma = sum over rows of dy * x_hat
+    dbeta  = sum over rows of dy.
+The ``*_f64`` functions take and return float64 arrays.  The others take bf16
+bit patterns, compute in float64 and round each bf16 output once at the end;
+mean and rstd are returned as float32.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .bf16 import round_to_bf16, to_f64
+
+
+def stats_f64(x: np.ndarray, eps: float):
+    """Two-pass mean and r = 1/sqrt(var + eps) per row of x [rows, H]."""
+    hidden = x.shape[-1]
+    mu = x.sum(axis=-1) / hidden
+    var = ((x - mu[:, None]) ** 2).sum(axis=-1) / hidden
+    r = 1.0 / np.sqrt(var + eps)
+    return mu, r
+
+
+def layernorm_fwd_f64(x, gamma, beta, eps: float):
+    """y, mu, r for x [rows, H], gamma [H], beta [H] (float64)."""
+    mu, r = stats_f64(x, eps)
+    x_hat = (x - mu[:, None]) * r[:, None]
+    return x_hat * gamma[None, :] + beta[None, :], mu, r
+
+
+def layernorm_bwd_f64(dy, x, gamma, eps: float):
+    """dx, dgamma, dbeta and the magnitude of dx's terms (float64)."""
+    mu, r = stats_f64(x, eps)
+    x_hat = (x - mu[:, None]) * r[:, None]
+    g = dy * gamma[None, :]
+    mean_g = g.mean(axis=-1)
+    mean_gx = (g * x_hat).mean(axis=-1)
+    dx = r[:, None] * (g - mean_g[:, None] - x_hat * mean_gx[:, None])
+    dgamma = (dy * x_hat).sum(axis=0)
+    dbeta = dy.sum(axis=0)
+    terms = r[:, None] * (np.abs(g) + np.abs(mean_g)[:, None] + np.abs(x_hat * mean_gx[:, None]))
+    return dx, dgamma, dbeta, terms
+
+
+def _eps64(eps: float) -> float:
+    """eps as the float32 value the GPU receives, widened exactly."""
+    return float(np.float32(eps))
+
+
+def layernorm_fwd(x_bits, gamma_bits, beta_bits, eps: float):
+    """y (bf16 bits), mean (float32), rstd (float32) for x [rows, H] (bf16 bits)."""
+    y, mu, r = layernorm_fwd_f64(to_f64(x_bits), to_f64(gamma_bits), to_f64(beta_bits), _eps64(eps))
+    return round_to_bf16(y), mu.astype(np.float32), r.astype(np.float32)
+
+
+def layernorm_bwd(dy_bits, x_bits, gamma_bits, eps: float, return_f64: bool = False):
+    """dx, dgamma, dbeta as bf16 bits.
+
+    Statistics are recomputed in float64 from x, not taken from the forward's
+    float32 outputs.  With ``return_f64`` the float64 results and term
+    magnitudes are returned too: (dx, dgamma, dbeta, dx_terms,
+    (sum|dy x_hat|, sum|dy|)).
+    """
+    x = to_f64(x_bits)
+    dy = to_f64(dy_bits)
+    eps64 = _eps64(eps)
+    dx, dgamma, dbeta, terms = layernorm_bwd_f64(dy, x, to_f64(gamma_bits), eps64)
+    out = (round_to_bf16(dx), round_to_bf16(dgamma), round_to_bf16(dbeta))
+    if not return_f64:
+        return out
+    mu, r = stats_f64(x, eps64)
+    x_hat = (x - mu[:, None]) * r[:, None]
+    col_terms = (np.abs(dy * x_hat).sum(axis=0), np.abs(dy).sum(axis=0))
+    return out, (dx, dgamma, dbeta, terms, col_terms)
