@@ -69,7 +69,7 @@ def softmax_fwd_f64(s, query_index, slope, scale: float):
 
 
 def softmax_bwd_f64(y, dy, query_index, scale: float):
-    """Backward on rows: returns (ds, magnitude of ds's terms), float64."""
+    """Backward on rows: returns (ds, condition magnitude |scale|*|y|*(|dy| + sum|y dy|))."""
     rows, length = y.shape
     i = np.asarray(query_index, dtype=np.int64)[:, None]
     j = np.arange(length, dtype=np.int64)[None, :]
@@ -78,7 +78,8 @@ def softmax_bwd_f64(y, dy, query_index, scale: float):
     dy = np.where(live, dy, 0.0)
     dot = (y * dy).sum(axis=-1, keepdims=True)
     ds = np.where(live, scale * y * (dy - dot), 0.0)
-    terms = np.where(live, abs(scale) * np.abs(y) * (np.abs(dy) + np.abs(dot)), 0.0)
+    abs_dot = np.abs(y * dy).sum(axis=-1, keepdims=True)
+    terms = np.where(live, abs(scale) * np.abs(y) * (np.abs(dy) + abs_dot), 0.0)
     return ds, terms
 
 
@@ -86,12 +87,13 @@ def _chunk_rows(seq: int) -> int:
     return max(1, (1 << 22) // seq)
 
 
-def softmax_fwd(scores_bits, slopes, scale: float, rows=None):
+def softmax_fwd(scores_bits, slopes, scale: float, rows=None, return_f64: bool = False):
     """Forward on [B, NH, L, L] scores (bf16 bits), or on selected flat rows.
 
     ``slopes`` are the float32 slopes of the NH heads; ``rows`` (optional)
     lists flat row numbers r = (b*NH + h)*L + i, and the result then has
-    shape [len(rows), L].  Output: bf16 bits.
+    shape [len(rows), L].  Output: bf16 bits (and, with ``return_f64``, the
+    unrounded float64 probabilities of the same rows).
     """
     b, nh, seq, seq2 = scores_bits.shape
     if seq != seq2:
@@ -101,12 +103,18 @@ def softmax_fwd(scores_bits, slopes, scale: float, rows=None):
     sl32 = np.asarray(slopes, dtype=np.float32).astype(np.float64)
     sc = float(np.float32(scale))
     out = np.empty((len(sel), seq), dtype=np.uint16)
+    vals = np.empty((len(sel), seq)) if return_f64 else None
     step = _chunk_rows(seq)
     for lo in range(0, len(sel), step):
         r = sel[lo: lo + step]
         y = softmax_fwd_f64(to_f64(flat[r]), r % seq, sl32[(r // seq) % nh], sc)
         out[lo: lo + len(r)] = round_to_bf16(y)
-    return out.reshape(scores_bits.shape) if rows is None else out
+        if return_f64:
+            vals[lo: lo + len(r)] = y
+    res = out.reshape(scores_bits.shape) if rows is None else out
+    if not return_f64:
+        return res
+    return res, (vals.reshape(scores_bits.shape) if rows is None else vals)
 
 
 def softmax_bwd(probs_bits, dprobs_bits, scale: float, rows=None, return_terms: bool = False):

@@ -39,10 +39,14 @@ def gelu_grad_terms(u):
     return np.abs(0.5 * (1.0 + t)) + np.abs(0.5 * u * (1.0 - t * t) * K * (1.0 + 3.0 * C * u * u))
 
 
-def bias_gelu_fwd(x_bits, bias_bits):
-    """y (bf16 bits) for x [rows, cols], bias [cols] (bf16 bits)."""
+def bias_gelu_fwd(x_bits, bias_bits, return_f64: bool = False):
+    """y (bf16 bits) for x [rows, cols], bias [cols] (bf16 bits).
+
+    With ``return_f64`` also returns the unrounded float64 y.
+    """
     u = to_f64(x_bits) + to_f64(bias_bits)[None, :]
-    return round_to_bf16(gelu(u))
+    y = gelu(u)
+    return (round_to_bf16(y), y) if return_f64 else round_to_bf16(y)
 
 
 def bias_gelu_bwd(dy_bits, x_bits, bias_bits, return_f64: bool = False):

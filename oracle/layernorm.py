@@ -42,7 +42,12 @@ def layernorm_fwd_f64(x, gamma, beta, eps: float):
 
 
 def layernorm_bwd_f64(dy, x, gamma, eps: float):
-    """dx, dgamma, dbeta and the magnitude of dx's terms (float64)."""
+    """dx, dgamma, dbeta and dx's condition magnitude (float64).
+
+    The magnitude r*(|g| + mean|g| + |x_hat|*mean|g*x_hat| + |mean(g*x_hat)|*r*|mu|)
+    bounds, times a few float32 units of roundoff per reduction level, the
+    error any float32 evaluation of dx can make.
+    """
     mu, r = stats_f64(x, eps)
     x_hat = (x - mu[:, None]) * r[:, None]
     g = dy * gamma[None, :]
@@ -51,7 +56,9 @@ def layernorm_bwd_f64(dy, x, gamma, eps: float):
     dx = r[:, None] * (g - mean_g[:, None] - x_hat * mean_gx[:, None])
     dgamma = (dy * x_hat).sum(axis=0)
     dbeta = dy.sum(axis=0)
-    terms = r[:, None] * (np.abs(g) + np.abs(mean_g)[:, None] + np.abs(x_hat * mean_gx[:, None]))
+    terms = r[:, None] * (np.abs(g) + np.abs(g).mean(axis=-1)[:, None]
+                          + np.abs(x_hat) * np.abs(g * x_hat).mean(axis=-1)[:, None]
+                          + (np.abs(mean_gx) * r * np.abs(mu))[:, None])
     return dx, dgamma, dbeta, terms
 
 
@@ -60,10 +67,24 @@ def _eps64(eps: float) -> float:
     return float(np.float32(eps))
 
 
-def layernorm_fwd(x_bits, gamma_bits, beta_bits, eps: float):
-    """y (bf16 bits), mean (float32), rstd (float32) for x [rows, H] (bf16 bits)."""
-    y, mu, r = layernorm_fwd_f64(to_f64(x_bits), to_f64(gamma_bits), to_f64(beta_bits), _eps64(eps))
-    return round_to_bf16(y), mu.astype(np.float32), r.astype(np.float32)
+def layernorm_fwd(x_bits, gamma_bits, beta_bits, eps: float, return_f64: bool = False):
+    """y (bf16 bits), mean (float32), rstd (float32) for x [rows, H] (bf16 bits).
+
+    With ``return_f64`` also returns (y, |gamma|*r*mean|x| + |x_hat*gamma| +
+    |beta|) in float64: the unrounded output and its condition magnitude (the
+    first term carries the rounding of the row mean through x - mu).
+    """
+    x = to_f64(x_bits)
+    gamma = to_f64(gamma_bits)
+    beta = to_f64(beta_bits)
+    y, mu, r = layernorm_fwd_f64(x, gamma, beta, _eps64(eps))
+    out = (round_to_bf16(y), mu.astype(np.float32), r.astype(np.float32))
+    if not return_f64:
+        return out
+    x_hat_gamma = y - beta[None, :]
+    terms = (np.abs(gamma)[None, :] * (r * np.abs(x).mean(axis=-1))[:, None] + np.abs(x_hat_gamma)
+             + np.abs(beta)[None, :])
+    return out, (y, terms)
 
 
 def layernorm_bwd(dy_bits, x_bits, gamma_bits, eps: float, return_f64: bool = False):
