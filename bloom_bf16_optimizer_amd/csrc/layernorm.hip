@@ -1,0 +1,351 @@
+// LayerNorm forward and backward for gfx950.
+//
+// What is computed: the fused LayerNorm of page "BLOOM 176B 训练技术概览",
+// section "融合 CUDA 核", also used as the embedding LayerNorm of "架构微调".
+// Per row of width H: mu = sum(x)/H, var = sum((x-mu)^2)/H,
+// r = 1/sqrt(var+eps), y = (x-mu)*r*gamma + beta; backward
+// dx = r*(g - mean(g) - x_hat*mean(g*x_hat)) with g = dy*gamma,
+// dgamma = sum_rows(dy*x_hat), dbeta = sum_rows(dy).
+//
+// Layout and mapping.  Rows are contiguous bf16; a "row team" of `tpr`
+// threads owns a row and each thread holds up to NV 16-byte vectors (8 bf16)
+// of it in registers, vector v = t + k*tpr (k < NV), so one row is read from
+// HBM exactly once with fully coalesced 16-byte loads.  tpr == 64 means one
+// wave per row (reductions in DPP, several rows per workgroup); otherwise the
+// whole workgroup is the team and reductions go wave -> LDS.
+//
+// The backward keeps per-thread FP32 column sums of dy*x_hat and dy for the
+// columns it owns while its team walks a strided set of rows, combines the
+// teams of a workgroup in LDS, and writes one FP32 partial row per workgroup;
+// colsum_kernel (colsum.hip) adds the partial rows in a fixed order.
+#include "device_common.h"
+#include "host_common.h"
+#include "launch_plan.h"
+
+namespace bloom {
+namespace {
+
+template <int NV, int MAXB>
+__global__ __launch_bounds__(MAXB) void ln_fwd_kernel(
+    const uint4* __restrict__ x, const uint4* __restrict__ gamma, const uint4* __restrict__ beta,
+    uint4* __restrict__ y, float* __restrict__ mean, float* __restrict__ rstd, int64_t rows,
+    int vecs, int tpr, float hidden, float eps) {
+  __shared__ float lds[kMaxWaves];
+  const bool wave_rows = (tpr == kWave);
+  const int t = wave_rows ? (int)(threadIdx.x & (kWave - 1)) : (int)threadIdx.x;
+  const int64_t row = wave_rows
+                          ? (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave
+                          : (int64_t)blockIdx.x;
+  if (row >= rows) return;  // uniform over the team
+  const int nwaves = blockDim.x / kWave;
+  const uint4* xr = x + row * vecs;
+
+  uint4 xv[NV], gv[NV], bv[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int v = t + k * tpr;
+    if (v < vecs) {
+      xv[k] = xr[v];
+      gv[k] = gamma[v];
+      bv[k] = beta[v];
+    } else {
+      xv[k] = make_uint4(0u, 0u, 0u, 0u);
+      gv[k] = xv[k];
+      bv[k] = xv[k];
+    }
+  }
+
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    float f[8];
+    unpack8(xv[k], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += f[e];
+  }
+  s = wave_rows ? wave_sum(s) : block_sum(s, lds, nwaves);
+  const float mu = s / hidden;
+
+  float q = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    if (t + k * tpr < vecs) {
+      float f[8];
+      unpack8(xv[k], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = f[e] - mu;
+        q = fmaf(d, d, q);
+      }
+    }
+  }
+  q = wave_rows ? wave_sum(q) : block_sum(q, lds, nwaves);
+  const float r = 1.0f / sqrtf(q / hidden + eps);
+
+  uint4* yr = y + row * vecs;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int v = t + k * tpr;
+    if (v < vecs) {
+      float f[8], g[8], b[8], o[8];
+      unpack8(xv[k], f);
+      unpack8(gv[k], g);
+      unpack8(bv[k], b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = fmaf((f[e] - mu) * r, g[e], b[e]);
+      yr[v] = pack8(o);
+    }
+  }
+  if (t == 0) {
+    mean[row] = mu;
+    rstd[row] = r;
+  }
+}
+
+// partial: [gridDim.x][2*H] fp32 -- dgamma partials then dbeta partials.
+// Dynamic LDS (wave mode with several teams only): 2*H floats.
+template <int NV, int MAXB>
+__global__ __launch_bounds__(MAXB) void ln_bwd_kernel(
+    const uint4* __restrict__ dy, const uint4* __restrict__ x, const uint4* __restrict__ gamma,
+    const float* __restrict__ mean, const float* __restrict__ rstd, uint4* __restrict__ dx,
+    float* __restrict__ partial, int64_t rows, int vecs, int tpr, float hidden) {
+  __shared__ float lds[2 * kMaxWaves];
+  extern __shared__ float combine[];
+  const bool wave_rows = (tpr == kWave);
+  const int teams = wave_rows ? (int)(blockDim.x / kWave) : 1;
+  const int team = wave_rows ? (int)(threadIdx.x / kWave) : 0;
+  const int t = wave_rows ? (int)(threadIdx.x & (kWave - 1)) : (int)threadIdx.x;
+  const int nwaves = blockDim.x / kWave;
+  const int64_t team_count = (int64_t)gridDim.x * teams;
+
+  uint4 gv[NV];
+  float dg[NV][8], db[NV][8];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int v = t + k * tpr;
+    gv[k] = (v < vecs) ? gamma[v] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      dg[k][e] = 0.f;
+      db[k][e] = 0.f;
+    }
+  }
+
+  // Software pipelining: the next row's dy and x are requested before the
+  // current row's reductions, so each team keeps two rows of loads in flight.
+  int64_t row = (int64_t)blockIdx.x * teams + team;
+  uint4 dv[NV], xv[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int v = t + k * tpr;
+    if (row < rows && v < vecs) {
+      dv[k] = dy[row * vecs + v];
+      xv[k] = x[row * vecs + v];
+    } else {
+      dv[k] = make_uint4(0u, 0u, 0u, 0u);
+      xv[k] = dv[k];
+    }
+  }
+  for (; row < rows; row += team_count) {
+    const int64_t next = row + team_count;
+    uint4 dn[NV], xn[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int v = t + k * tpr;
+      if (next < rows && v < vecs) {
+        dn[k] = dy[next * vecs + v];
+        xn[k] = x[next * vecs + v];
+      } else {
+        dn[k] = make_uint4(0u, 0u, 0u, 0u);
+        xn[k] = dn[k];
+      }
+    }
+    const float mu = mean[row];
+    const float r = rstd[row];
+    // sums of g and g*x_hat (out-of-range vectors are zero and add nothing)
+    float sg = 0.f, sgx = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      float d[8], f[8], g[8];
+      unpack8(dv[k], d);
+      unpack8(xv[k], f);
+      unpack8(gv[k], g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float gg = d[e] * g[e];
+        const float xh = (f[e] - mu) * r;
+        sg += gg;
+        sgx = fmaf(gg, xh, sgx);
+      }
+    }
+    if (wave_rows) {
+      wave_sum2(sg, sgx);
+    } else {
+      block_sum2(sg, sgx, lds, nwaves);
+    }
+    const float mg = sg / hidden;
+    const float mgx = sgx / hidden;
+    uint4* dxr = dx + row * vecs;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int v = t + k * tpr;
+      if (v < vecs) {
+        float d[8], f[8], g[8], o[8];
+        unpack8(dv[k], d);
+        unpack8(xv[k], f);
+        unpack8(gv[k], g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xh = (f[e] - mu) * r;
+          o[e] = r * (d[e] * g[e] - mg - xh * mgx);
+          dg[k][e] = fmaf(d[e], xh, dg[k][e]);
+          db[k][e] += d[e];
+        }
+        dxr[v] = pack8(o);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      dv[k] = dn[k];
+      xv[k] = xn[k];
+    }
+  }
+
+  const int hidden_i = vecs * 8;
+  float* out = partial + (int64_t)blockIdx.x * 2 * hidden_i;
+  if (teams == 1) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int v = t + k * tpr;
+      if (v < vecs) {
+        float4* og = reinterpret_cast<float4*>(out + v * 8);
+        float4* ob = reinterpret_cast<float4*>(out + hidden_i + v * 8);
+        og[0] = make_float4(dg[k][0], dg[k][1], dg[k][2], dg[k][3]);
+        og[1] = make_float4(dg[k][4], dg[k][5], dg[k][6], dg[k][7]);
+        ob[0] = make_float4(db[k][0], db[k][1], db[k][2], db[k][3]);
+        ob[1] = make_float4(db[k][4], db[k][5], db[k][6], db[k][7]);
+      }
+    }
+    return;
+  }
+  // Several wave-teams: add them in team order in LDS, then write one row.
+  for (int turn = 0; turn < teams; ++turn) {
+    if (team == turn) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int v = t + k * tpr;
+        if (v < vecs) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int c = v * 8 + e;
+            combine[c] = (turn == 0) ? dg[k][e] : combine[c] + dg[k][e];
+            combine[hidden_i + c] = (turn == 0) ? db[k][e] : combine[hidden_i + c] + db[k][e];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  for (int c = threadIdx.x * 4; c < 2 * hidden_i; c += blockDim.x * 4)
+    *reinterpret_cast<float4*>(out + c) = *reinterpret_cast<const float4*>(combine + c);
+}
+
+template <int NV, int MAXB>
+void launch_fwd(const RowPlan& p, hipStream_t s, const uint4* x, const uint4* g, const uint4* b,
+                uint4* y, float* mean, float* rstd, int64_t rows, int vecs, float eps) {
+  hipLaunchKernelGGL((ln_fwd_kernel<NV, MAXB>), dim3(p.grid), dim3(p.block), 0, s, x, g, b, y, mean, rstd,
+                     rows, vecs, p.tpr, (float)(vecs * 8), eps);
+}
+
+template <int NV, int MAXB>
+void launch_bwd(const RowPlan& p, hipStream_t s, const uint4* dy, const uint4* x, const uint4* g,
+                const float* mean, const float* rstd, uint4* dx, float* partial, int64_t rows,
+                int vecs, size_t lds_bytes) {
+  hipLaunchKernelGGL((ln_bwd_kernel<NV, MAXB>), dim3(p.grid), dim3(p.block), lds_bytes, s, dy, x, g, mean,
+                     rstd, dx, partial, rows, vecs, p.tpr, (float)(vecs * 8));
+}
+
+bloom_status check_rows(int64_t rows, int64_t hidden) {
+  BLOOM_REQUIRE(rows >= 0, BLOOM_ERR_SHAPE, "rows = %lld is negative", (long long)rows);
+  BLOOM_REQUIRE(hidden >= 8 && hidden <= BLOOM_MAX_HIDDEN && hidden % 8 == 0, BLOOM_ERR_SHAPE,
+                "hidden = %lld must be a multiple of 8 in [8, %d]", (long long)hidden,
+                BLOOM_MAX_HIDDEN);
+  BLOOM_REQUIRE(rows <= (int64_t(1) << 40) / hidden, BLOOM_ERR_SHAPE, "rows*hidden too large");
+  return BLOOM_OK;
+}
+
+}  // namespace
+}  // namespace bloom
+
+using namespace bloom;
+
+extern "C" bloom_status bloom_layernorm_fwd(const bloom_bf16* x, const bloom_bf16* gamma,
+                                            const bloom_bf16* beta, bloom_bf16* y, float* mean,
+                                            float* rstd, int64_t rows, int64_t hidden, float eps,
+                                            hipStream_t stream) {
+  clear_error();
+  if (bloom_status st = check_rows(rows, hidden)) return st;
+  BLOOM_REQUIRE(eps > 0.f && eps < INFINITY, BLOOM_ERR_HPARAM, "eps must be positive and finite");
+  if (rows == 0) return BLOOM_OK;
+  BLOOM_REQUIRE_PTR(x);
+  BLOOM_REQUIRE_PTR(gamma);
+  BLOOM_REQUIRE_PTR(beta);
+  BLOOM_REQUIRE_PTR(y);
+  BLOOM_REQUIRE_PTR(mean);
+  BLOOM_REQUIRE_PTR(rstd);
+  const int vecs = (int)(hidden / 8);
+  const RowPlan p = plan_rows_fwd(rows, vecs);
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const uint4* gv = reinterpret_cast<const uint4*>(gamma);
+  const uint4* bv = reinterpret_cast<const uint4*>(beta);
+  uint4* yv = reinterpret_cast<uint4*>(y);
+#define CALL(NV, MAXB) launch_fwd<NV, MAXB>(p, stream, xv, gv, bv, yv, mean, rstd, rows, vecs, eps)
+  BLOOM_ROW_DISPATCH(p, CALL);
+#undef CALL
+  return launch_status("bloom_layernorm_fwd");
+}
+
+extern "C" size_t bloom_layernorm_bwd_workspace_size(int64_t rows, int64_t hidden) {
+  if (rows <= 0 || hidden <= 0 || hidden % 8 != 0 || hidden > BLOOM_MAX_HIDDEN) return 0;
+  const RowPlan p = plan_rows_bwd(rows, (int)(hidden / 8), device_cu_count());
+  return (size_t)p.grid * 2 * (size_t)hidden * sizeof(float);
+}
+
+extern "C" bloom_status bloom_layernorm_bwd(const bloom_bf16* dy, const bloom_bf16* x,
+                                            const bloom_bf16* gamma, const float* mean,
+                                            const float* rstd, bloom_bf16* dx, bloom_bf16* dgamma,
+                                            bloom_bf16* dbeta, void* workspace,
+                                            size_t workspace_bytes, int64_t rows, int64_t hidden,
+                                            hipStream_t stream) {
+  clear_error();
+  if (bloom_status st = check_rows(rows, hidden)) return st;
+  if (rows == 0) return BLOOM_OK;
+  BLOOM_REQUIRE_PTR(dy);
+  BLOOM_REQUIRE_PTR(x);
+  BLOOM_REQUIRE_PTR(gamma);
+  BLOOM_REQUIRE_PTR(mean);
+  BLOOM_REQUIRE_PTR(rstd);
+  BLOOM_REQUIRE_PTR(dx);
+  BLOOM_REQUIRE_PTR(dgamma);
+  BLOOM_REQUIRE_PTR(dbeta);
+  BLOOM_REQUIRE(workspace != nullptr, BLOOM_ERR_WORKSPACE, "workspace is NULL");
+  BLOOM_REQUIRE(aligned16(workspace), BLOOM_ERR_ALIGN, "workspace is not 16-byte aligned");
+  const int vecs = (int)(hidden / 8);
+  const RowPlan p = plan_rows_bwd(rows, vecs, device_cu_count());
+  const size_t need = (size_t)p.grid * 2 * (size_t)hidden * sizeof(float);
+  BLOOM_REQUIRE(workspace_bytes >= need, BLOOM_ERR_WORKSPACE,
+                "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  float* partial = static_cast<float*>(workspace);
+  const size_t lds = (p.tpr == kWave && p.block > kWave) ? 2 * (size_t)hidden * sizeof(float) : 0;
+  const uint4* dyv = reinterpret_cast<const uint4*>(dy);
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const uint4* gv = reinterpret_cast<const uint4*>(gamma);
+  uint4* dxv = reinterpret_cast<uint4*>(dx);
+#define CALL(NV, MAXB) \
+  launch_bwd<NV, MAXB>(p, stream, dyv, xv, gv, mean, rstd, dxv, partial, rows, vecs, lds)
+  BLOOM_ROW_DISPATCH(p, CALL);
+#undef CALL
+  if (bloom_status st = launch_status("bloom_layernorm_bwd")) return st;
+  launch_colsum(partial, p.grid, 2 * hidden, hidden, dgamma, dbeta, stream);
+  return launch_status("bloom_layernorm_bwd column sums");
+}

@@ -1,0 +1,216 @@
+/*
+ * bloom_kernels.h -- C ABI of the BLOOM fused kernels and BF16Optimizer step
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed comes from four pages on how BLOOM-176B was trained with
+ * Megatron-DeepSpeed:
+ *   [overview]  "BLOOM 176B 训练技术概览"
+ *   [ru]        "Как обучали BLOOM: технологии Megatron и DeepSpeed для 176-миллиардной модели"
+ *   [3d]        "企业官网建设流程全解析" (its body covers BLOOM's 3-D parallelism,
+ *               ZeRO, BF16 and fused kernels despite the title)
+ *   [mini]      "单机多卡实战：Megatron-DeepSpeed训练类BLOOM模型全流程解析"
+ * Each entry point below names the section it implements.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are raw DEVICE pointers to caller-owned memory (e.g. allocated by
+ *   PyTorch).  The library never allocates, frees or synchronises; a call only
+ *   validates its arguments and enqueues kernels on `stream` (NULL = the
+ *   default stream).  Outputs are complete once the stream reaches that point.
+ * - bf16 values are raw bfloat16 bit patterns (`bloom_bf16`).  All arithmetic
+ *   is FP32 (FP64 for the gradient-norm sum); bf16 outputs are rounded to
+ *   nearest, ties to even.
+ * - Matrices are row-major and contiguous.  Every array pointer must be
+ *   16-byte aligned, and row widths (hidden, cols, seq) must be multiples of 8
+ *   so that every row starts on a 16-byte boundary.
+ * - Outputs must not overlap inputs (no in-place operation) unless stated.
+ * - Validation happens before anything is enqueued: on any error the function
+ *   returns a non-zero status, enqueues nothing, and bloom_last_error() holds a
+ *   message (thread-local).  A launch failure reported by the HIP runtime
+ *   returns BLOOM_ERR_HIP; faults inside a kernel surface at the caller's next
+ *   synchronisation.  Empty inputs (rows == 0, n == 0, batch*heads == 0) return
+ *   BLOOM_OK and enqueue nothing.
+ * - Results are bitwise deterministic run to run on one device type: every
+ *   reduction has a fixed order that depends only on the shape.
+ */
+#ifndef BLOOM_KERNELS_H
+#define BLOOM_KERNELS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t bloom_bf16; /* raw bfloat16 bits */
+
+typedef enum {
+  BLOOM_OK = 0,
+  BLOOM_ERR_NULL = 1,      /* a required pointer is NULL */
+  BLOOM_ERR_SHAPE = 2,     /* a size is negative, too large, or not a multiple of 8 */
+  BLOOM_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
+  BLOOM_ERR_WORKSPACE = 4, /* workspace missing or smaller than the *_workspace_size query */
+  BLOOM_ERR_HPARAM = 5,    /* a scalar argument is out of range */
+  BLOOM_ERR_HIP = 6        /* the HIP runtime reported an error */
+} bloom_status;
+
+/* Version of this ABI (incremented on any signature change). */
+int bloom_abi_version(void);
+/* Static text for a status code. */
+const char* bloom_status_string(int status);
+/* Detail of the last failing call on this thread ("" if none). */
+const char* bloom_last_error(void);
+
+/* Largest supported row width of the LayerNorm and bias-GeLU kernels, and
+ * largest softmax sequence length. */
+#define BLOOM_MAX_HIDDEN 65536
+#define BLOOM_MAX_SEQ 16384
+#define BLOOM_MAX_HEADS 256
+
+/* ---------------------------------------------------------------------------
+ * LayerNorm forward.  [overview] "融合 CUDA 核" (the fused LayerNorm kernel)
+ * and "架构微调" (the embedding LayerNorm after the word embedding: same call
+ * on embedding rows); [3d] 4.3.
+ *   per row:  mu = sum(x)/H,  var = sum((x-mu)^2)/H,  r = 1/sqrt(var+eps),
+ *             y = (x-mu)*r*gamma + beta
+ * x, y    [rows, hidden] bf16;  gamma, beta [hidden] bf16;
+ * mean, rstd [rows] fp32 (saved for the backward).
+ * hidden: 8 .. BLOOM_MAX_HIDDEN, multiple of 8.  eps > 0.
+ */
+bloom_status bloom_layernorm_fwd(const bloom_bf16* x, const bloom_bf16* gamma,
+                                 const bloom_bf16* beta, bloom_bf16* y, float* mean,
+                                 float* rstd, int64_t rows, int64_t hidden, float eps,
+                                 hipStream_t stream);
+
+/* Bytes of workspace bloom_layernorm_bwd needs for its column partial sums. */
+size_t bloom_layernorm_bwd_workspace_size(int64_t rows, int64_t hidden);
+
+/* LayerNorm backward.  [overview] "融合 CUDA 核".
+ *   x_hat = (x-mean)*rstd,  g = dy*gamma,
+ *   dx     = rstd * (g - mean_row(g) - x_hat * mean_row(g*x_hat))
+ *   dgamma = sum_rows(dy * x_hat),   dbeta = sum_rows(dy)
+ * dy, x, dx [rows, hidden] bf16; gamma [hidden] bf16; mean, rstd [rows] fp32
+ * from bloom_layernorm_fwd; dgamma, dbeta [hidden] bf16 (written, not added
+ * to).  workspace: device memory of at least
+ * bloom_layernorm_bwd_workspace_size(rows, hidden) bytes, 16-byte aligned,
+ * owned by the caller; its contents on entry do not matter.
+ */
+bloom_status bloom_layernorm_bwd(const bloom_bf16* dy, const bloom_bf16* x,
+                                 const bloom_bf16* gamma, const float* mean,
+                                 const float* rstd, bloom_bf16* dx, bloom_bf16* dgamma,
+                                 bloom_bf16* dbeta, void* workspace, size_t workspace_bytes,
+                                 int64_t rows, int64_t hidden, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * ALiBi slopes (host only, no device work).  [overview] "架构微调" (ALiBi
+ * replaces position embeddings) and "资源" (the ALiBi paper, arXiv:2108.12409,
+ * whose rule this is): n heads, n a power of two -> head h (1-based) has
+ * slope 2^(-8h/n); otherwise the c = 2^floor(log2 n) slopes of that rule
+ * followed by the 1st, 3rd, 5th, ... slopes of the rule for 2c, n-c of them.
+ * Computed in FP64, rounded once to FP32.  Writes the slopes of heads
+ * head_offset .. head_offset+heads-1 to out_host (HOST memory, `heads` floats).
+ */
+bloom_status bloom_alibi_slopes(int32_t total_heads, int32_t head_offset, int32_t heads,
+                                float* out_host);
+
+/* Scale + ALiBi bias + causal mask + softmax, forward.  [overview] "融合 CUDA
+ * 核" (the combined scale/mask/softmax kernel) with the ALiBi bias of
+ * "架构微调"; [3d] 4.3 (trained at 2048, run at 8192).
+ * For every (b, h, query i) row of the [batch, heads, seq, seq] scores:
+ *   z_j = scale*s_ij - slope_h*(i-j)  (j <= i),   y_j = softmax_j(z)   (j <= i),
+ *   y_j = +0 for j > i.   Score entries with j > i are never read.
+ * slope_h is head (head_offset + h) of a model with total_heads heads (the
+ * tensor-parallel rank's slice).  seq: 8 .. BLOOM_MAX_SEQ, multiple of 8;
+ * heads <= BLOOM_MAX_HEADS; scale finite.
+ */
+bloom_status bloom_alibi_softmax_fwd(const bloom_bf16* scores, bloom_bf16* probs,
+                                     int64_t batch, int32_t heads, int64_t seq,
+                                     int32_t head_offset, int32_t total_heads, float scale,
+                                     hipStream_t stream);
+
+/* Backward of bloom_alibi_softmax_fwd with respect to the raw scores:
+ *   ds_j = scale * y_j * (dy_j - sum_{k<=i} y_k dy_k)   (j <= i),  +0 for j > i.
+ * probs = the forward output y, dprobs = dy, dscores = ds, all
+ * [batch, heads, seq, seq] bf16.  Entries with j > i are never read.
+ */
+bloom_status bloom_alibi_softmax_bwd(const bloom_bf16* probs, const bloom_bf16* dprobs,
+                                     bloom_bf16* dscores, int64_t batch, int32_t heads,
+                                     int64_t seq, float scale, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * bias + GeLU forward.  [overview] "融合 CUDA 核" (bias + GeLU fusion); the
+ * MLP's GeLU(XA) of [3d] 2.1.  tanh form (Hendrycks and Gimpel,
+ * arXiv:1606.08415):  u = x + bias (FP32),
+ *   y = u/2 * (1 + tanh(sqrt(2/pi) * (u + 0.044715 u^3)))
+ * x, y [rows, cols] bf16; bias [cols] bf16.  cols: 8 .. BLOOM_MAX_HIDDEN,
+ * multiple of 8.
+ */
+bloom_status bloom_bias_gelu_fwd(const bloom_bf16* x, const bloom_bf16* bias, bloom_bf16* y,
+                                 int64_t rows, int64_t cols, hipStream_t stream);
+
+/* Bytes of workspace bloom_bias_gelu_bwd needs for its column partial sums. */
+size_t bloom_bias_gelu_bwd_workspace_size(int64_t rows, int64_t cols);
+
+/* bias + GeLU backward:  dx = dy * gelu'(x + bias),  dbias = sum_rows(dx)
+ * (dbias sums the unrounded FP32 dx).  dy, x, dx [rows, cols] bf16; bias,
+ * dbias [cols] bf16 (dbias written, not added to).  workspace as for
+ * bloom_layernorm_bwd, sized by bloom_bias_gelu_bwd_workspace_size.
+ */
+bloom_status bloom_bias_gelu_bwd(const bloom_bf16* dy, const bloom_bf16* x,
+                                 const bloom_bf16* bias, bloom_bf16* dx, bloom_bf16* dbias,
+                                 void* workspace, size_t workspace_bytes, int64_t rows,
+                                 int64_t cols, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * BF16Optimizer, stage 1: FP32 gradient accumulation across pipeline
+ * micro-batches.  [overview] "BF16 优化器"; 32 accumulation steps in [3d] 3.3.
+ *   first_microbatch != 0:  grad_acc[i] = float(grad[i])
+ *   first_microbatch == 0:  grad_acc[i] = grad_acc[i] + float(grad[i])  (one FP32 add)
+ * grad_acc [n] fp32 (read-modify-write), grad [n] bf16.  Any n >= 0.
+ */
+bloom_status bloom_bf16_grad_accumulate(float* grad_acc, const bloom_bf16* grad, int64_t n,
+                                        int32_t first_microbatch, hipStream_t stream);
+
+/* Hyperparameters of bloom_bf16_adamw_step, as FP64; the library derives every
+ * FP32 kernel constant from them in FP64 and rounds each once. */
+typedef struct {
+  double lr;            /* >= 0; [3d] 3.3 and [mini] 3 use 6e-5 */
+  double beta1;         /* in [0, 1) */
+  double beta2;         /* in [0, 1) */
+  double eps;           /* > 0 */
+  double weight_decay;  /* >= 0; [3d] 3.3 and [mini] 3 use 0.01 */
+  double max_grad_norm; /* > 0; [3d] 4.3 and [mini] 3 use 1.0 */
+  int64_t step;         /* t >= 1 of this update (bias correction 1 - beta^t) */
+} bloom_adamw_hparams;
+
+/* Bytes of workspace bloom_bf16_adamw_step needs (norm partials and the
+ * clip coefficient). */
+size_t bloom_bf16_adamw_workspace_size(int64_t n);
+
+/* BF16Optimizer, stages 2-5, in one call: global L2 norm of the accumulated
+ * gradient (FP64 sum), clip coefficient, AdamW on the FP32 master weights and
+ * moments, and the bf16 parameter copy.  [overview] "BF16 优化器"; [3d] 1 (FP32
+ * master, momentum and variance), 3.3 (AdamW, lr, weight decay), 4.3 (global
+ * norm clipped at 1.0); [mini] 3.
+ *   N = sqrt(sum acc^2);  c = max_grad_norm/N if N > max_grad_norm else 1
+ *   g = c*acc;  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2
+ *   master -= lr * ( (m/(1-b1^t)) / (sqrt(v/(1-b2^t)) + eps) + weight_decay*master )
+ *   param_bf16 = round-to-nearest-even(master)
+ * master, exp_avg, exp_avg_sq [n] fp32 (updated in place); grad_acc [n] fp32
+ * (read only); param_bf16 [n] bf16 (written).  grad_norm_out: optional device
+ * pointer to one float that receives N (NULL to skip).  A NaN norm leaves
+ * c = 1; an infinite norm gives c = 0.  The norm and c never leave the device.
+ * workspace: device memory of bloom_bf16_adamw_workspace_size(n) bytes.
+ */
+bloom_status bloom_bf16_adamw_step(float* master, float* exp_avg, float* exp_avg_sq,
+                                   bloom_bf16* param_bf16, const float* grad_acc, int64_t n,
+                                   const bloom_adamw_hparams* hp, float* grad_norm_out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLOOM_KERNELS_H */
