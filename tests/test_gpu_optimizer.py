@@ -125,10 +125,11 @@ def test_two_steps_and_checkpoint_round_trip():
     z = np.zeros(n, dtype=np.float32)
     a1 = acc1.cpu().numpy()
     a2 = acc2.cpu().numpy()
-    (p1, m1, v1, _), _, _, _ = _oracle_step(p, z, z, a1, 1)
+    (p1, m1, v1, _), f64_1, terms_1, _ = _oracle_step(p, z, z, a1, 1)
+    for got, ref, tm_, nm in zip(saved, f64_1, terms_1, ("master", "exp_avg", "exp_avg_sq")):
+        check_state(f"step 1 {nm}", got.numpy(), ref, tm_)
     (p2, m2, v2, pb2), f64, terms, _ = _oracle_step(saved[0].numpy(), saved[1].numpy(), saved[2].numpy(), a2, 2)
     _compare_step("step 2", after_a[0], after_a[1], after_a[2], host_bf16(param_a), f64, terms, pb2)
-    check_state("step 1 master", saved[0].numpy(), p1.astype(np.float64), np.abs(p1).astype(np.float64) * 2)
 
 
 def test_bf16_copy_rounding_table():

@@ -41,6 +41,33 @@ def test_derivative_finite_differences_and_autograd():
     assert np.allclose(G.gelu_grad(u), tu.grad.numpy(), rtol=1e-13, atol=1e-14)
 
 
+def _tanh_form_50_digits(u: float):
+    """u/2 (1 + tanh a) and its derivative, evaluated in 120-digit decimal from
+    the tanh form itself (tanh a = (e^2a - 1)/(e^2a + 1))."""
+    from decimal import Decimal as D, getcontext
+    getcontext().prec = 120
+    k = D(2) / D("3.14159265358979323846264338327950288419716939937510")
+    k = k.sqrt()
+    c = D("0.044715")
+    x = D(u)
+    a = k * (x + c * x ** 3)
+    e2 = (2 * a).exp()
+    t = (e2 - 1) / (e2 + 1)
+    y = x / 2 * (1 + t)
+    dy = (1 + t) / 2 + x / 2 * (1 - t * t) * k * (1 + 3 * c * x * x)
+    return float(y), float(dy)
+
+
+def test_far_tails_against_120_digit_tanh_form():
+    # float64 1 + tanh(a) is exactly 0 for a < -19; the oracle must still give the
+    # true tiny values there (e.g. gelu(-10) = -1.2e-37, a normal bf16 number)
+    for u in (-12.0, -10.0, -9.95, -7.0, -5.0, -1.0, -0.75, 0.5, 3.0, 9.0):
+        y, dy = _tanh_form_50_digits(u)
+        assert abs(G.gelu(np.array([u]))[0] - y) <= 1e-13 * abs(y) + 1e-300, u
+        assert abs(G.gelu_grad(np.array([u]))[0] - dy) <= 1e-12 * abs(dy) + 1e-300, u
+    assert G.gelu(np.array([-10.0]))[0] < -1e-37
+
+
 def test_bias_broadcast_and_dbias():
     rng = np.random.default_rng(12)
     x = round_to_bf16(rng.standard_normal((48, 96)))
