@@ -61,7 +61,8 @@ def bytes_model(sh, n, mb):
         "bias_gelu_bwd": grows * gcols * 6 + gcols * 4,
         "grad_accumulate_first": n * 6,
         "grad_accumulate": n * 10,
-        "adamw_step": n * 34,   # norm pass reads acc (4 B); update reads 16 B, writes 14 B
+        "grad_accumulate_last": n * 10,  # also emits the norm's FP64 partials (1/1024 of a double per element)
+        "adamw_step": n * 30,   # update reads acc, master, m, v (16 B), writes master, m, v, bf16 (14 B)
     }
 
 
@@ -164,7 +165,7 @@ def run_gpu(args):
     log(f"bench: resident {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
 
     names = ["layernorm_fwd", "alibi_softmax_fwd", "bias_gelu_fwd", "bias_gelu_bwd", "alibi_softmax_bwd",
-             "layernorm_bwd", "grad_accumulate_first", "grad_accumulate", "adamw_step"]
+             "layernorm_bwd", "grad_accumulate_first", "grad_accumulate", "grad_accumulate_last", "adamw_step"]
     ev = {k: [] for k in names}
 
     def timed(name, fn, record):
@@ -189,10 +190,15 @@ def run_gpu(args):
         timed("layernorm_bwd", lambda: ops.bloom_layernorm_bwd(ln_dy, ln_x2, ln_g, ln_mean2, ln_rstd2, ln_dx,
                                                                ln_dg, ln_db, ln_ws), record)
         for k in range(mb):
-            name = "grad_accumulate_first" if k == 0 else "grad_accumulate"
             g = grads[k % GRAD_BUFFERS]
-            timed(name, lambda g=g, k=k: ops.bloom_bf16_grad_accumulate(acc, g, k == 0), record)
-        hp = ops.adamw_hparams(W.LR, W.BETA1, W.BETA2, W.ADAM_EPS, W.WEIGHT_DECAY, W.MAX_GRAD_NORM, t)
+            if k == mb - 1:   # the last micro-batch also writes the norm's partial sums
+                timed("grad_accumulate_last", lambda g=g, k=k: ops.bloom_bf16_grad_accumulate_sumsq(
+                    acc, g, k == 0, opt_ws), record)
+            else:
+                name = "grad_accumulate_first" if k == 0 else "grad_accumulate"
+                timed(name, lambda g=g, k=k: ops.bloom_bf16_grad_accumulate(acc, g, k == 0), record)
+        hp = ops.adamw_hparams(W.LR, W.BETA1, W.BETA2, W.ADAM_EPS, W.WEIGHT_DECAY, W.MAX_GRAD_NORM, t,
+                               sumsq_in_workspace=True)
         timed("adamw_step", lambda: ops.bloom_bf16_adamw_step(master, exp_avg, exp_avg_sq, param, acc, hp, norm,
                                                               opt_ws), record)
 
@@ -282,7 +288,7 @@ def run_cpu_baseline(min_seconds_per_row: float = 1.5):
         clock("grad_accumulate", n * 10, lambda: oopt.grad_accumulate(acc, g2, False))
         p = synth.tensor(4, W.S_OPT_PARAM, n, 0.02)
         z = np.zeros(n, dtype=np.float32)
-        clock("adamw_step", n * 34, lambda: oopt.bf16_optimizer_step(
+        clock("adamw_step", n * 30, lambda: oopt.bf16_optimizer_step(
             p, z, z, acc, W.LR, W.BETA1, W.BETA2, W.ADAM_EPS, W.WEIGHT_DECAY, W.MAX_GRAD_NORM, 1))
     return r
 
@@ -301,9 +307,10 @@ def main():
         sys.exit(2)
 
     ms_step, per, bts, n, mb = run_gpu(args)
-    nfirst, nrest = 1, mb - 1
+    nfirst, nrest = 1, mb - 2
     step_bytes = (sum(bts[k] for k in ("layernorm_fwd", "layernorm_bwd", "alibi_softmax_fwd",
-                                       "alibi_softmax_bwd", "bias_gelu_fwd", "bias_gelu_bwd", "adamw_step"))
+                                       "alibi_softmax_bwd", "bias_gelu_fwd", "bias_gelu_bwd", "adamw_step",
+                                       "grad_accumulate_last"))
                   + nfirst * bts["grad_accumulate_first"] + nrest * bts["grad_accumulate"])
     kernels = {}
     for k, ms in per.items():
@@ -334,7 +341,7 @@ def main():
                    "storage": "bf16 activations and gradients, fp32 master/moments/accumulator"},
         "adamw_step_ms": round(per["adamw_step"], 3),
         "kernels": kernels,
-        "roofline": {"kernel": "grad_accumulate (micro-batches 2-32)", "bound": "hbm",
+        "roofline": {"kernel": "grad_accumulate (micro-batches 2-31)", "bound": "hbm",
                      "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
@@ -348,6 +355,8 @@ def main():
                   "bias_gelu_bwd", "adamw_step"):
             bb, s = r[k]
             cpu_step_s += bts[k] / (bb / s)
+        bb, s = r["grad_accumulate"]
+        cpu_step_s += bts["grad_accumulate_last"] / (bb / s)
         bb, s = r["grad_accumulate_first"]
         cpu_step_s += nfirst * bts["grad_accumulate_first"] / (bb / s)
         bb, s = r["grad_accumulate"]
@@ -356,7 +365,8 @@ def main():
             "value": round(step_bytes / cpu_step_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": "NumPy float64 oracle, one thread: 64 LayerNorm rows and 64 bias-GeLU rows of width "
                       "14336, 128 softmax rows of length 2048 spread over the 28 heads, 4.2M optimizer elements "
-                      "(one first and one later accumulation, one norm+clip+AdamW+bf16 step), each repeated "
+                      "(one first and one later accumulation, one norm+clip+AdamW+bf16 step, credited with the step's "
+                      "30 B/element), each repeated "
                       "for >= 1.5 s; each row's oracle rate is scaled to that row's bytes in the step "
                       f"({time.perf_counter() - t0:.1f} s of CPU time in all)",
             "step_seconds_extrapolated": round(cpu_step_s, 1)}

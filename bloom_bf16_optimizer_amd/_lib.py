@@ -25,7 +25,8 @@ c_size = ctypes.c_size_t
 class AdamWHParams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
                 ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
-                ("max_grad_norm", ctypes.c_double), ("step", ctypes.c_int64)]
+                ("max_grad_norm", ctypes.c_double), ("step", ctypes.c_int64),
+                ("sumsq_in_workspace", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 # name -> (restype, argtypes)
@@ -46,6 +47,8 @@ SIGNATURES = {
     "bloom_bias_gelu_bwd": (ctypes.c_int, [c_void_p] * 6 + [c_size, c_i64, c_i64, c_void_p]),
     "bloom_bf16_grad_accumulate": (ctypes.c_int, [c_void_p, c_void_p, c_i64, c_i32, c_void_p]),
     "bloom_bf16_adamw_workspace_size": (c_size, [c_i64]),
+    "bloom_bf16_grad_accumulate_sumsq": (ctypes.c_int, [c_void_p, c_void_p, c_i64, c_i32, c_void_p, c_size,
+                                                        c_void_p]),
     "bloom_bf16_adamw_step": (ctypes.c_int, [c_void_p] * 5 + [c_i64, ctypes.POINTER(AdamWHParams), c_void_p,
                                              c_void_p, c_size, c_void_p]),
 }

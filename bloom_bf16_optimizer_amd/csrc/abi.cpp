@@ -53,7 +53,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int bloom_abi_version(void) { return 1; }
+int bloom_abi_version(void) { return 2; }
 
 const char* bloom_status_string(int status) {
   switch (status) {

@@ -10,17 +10,23 @@
 // clipped at global norm 1.0); page "单机多卡实战：Megatron-DeepSpeed训练类BLOOM
 // 模型全流程解析", section 3 (the same lr, weight decay, clip and bf16 flags).
 //
-// All passes are flat, elementwise streams over n elements: 16-byte bf16
-// vectors (8 elements) against pairs of 16-byte fp32 vectors, grid-stride
-// loops with kUnroll groups of loads issued before any store, 64-bit indices
-// (n reaches 3.67e9), and an n % 8 tail handled by the first threads.
+// Launch shape.  Every pass is a flat stream: one workgroup of 256 threads per
+// 1024 consecutive elements, each thread one "quad" of 4 elements, so every
+// wave-wide load or store instruction covers one contiguous span (512 B of
+// bf16, 1 KiB of fp32).  Workgroup ids go round-robin over the 8 XCDs; the
+// logical block is remapped so that each XCD sweeps one contiguous eighth of
+// the arrays.  Indices are 64-bit (n reaches 3.67e9); a trailing partial quad
+// is handled element by element.  Measured on MI355X this shape streams ~6
+// TB/s where grid-stride loops with two 16-byte vectors per thread stay near 5.
 //
-// The norm is summed in FP64 (per-thread fused multiply-adds over exact
-// float -> double widenings, four interleaved accumulators), reduced per
-// workgroup, and the workgroup partials are added in workgroup order by a
-// one-workgroup finalize kernel that also forms the clip coefficient.  The
-// coefficient stays in device memory; the AdamW kernel reads it, so the step
-// has no host round trip.
+// Norm.  Every workgroup writes the FP64 sum of acc^2 over its 1024 elements
+// (exact float -> double widening, fused multiply-adds) to partials[logical
+// block]; the partials are then added in a fixed order by a 256-workgroup
+// pass and a one-workgroup finalize that forms N and the clip coefficient c,
+// which stay in device memory for the AdamW kernel (no host round trip).  The
+// partials come either from a standalone read of acc or, with no extra
+// traffic, from the last micro-batch's accumulation pass.  The per-block
+// partials are identical either way, so both paths give the same bits.
 #include <cmath>
 
 #include "device_common.h"
@@ -29,96 +35,111 @@
 namespace bloom {
 namespace {
 
-constexpr int kBlock = 256;
-constexpr int kUnroll = 2;
-constexpr int kNormBlocksPerCu = 8;
+constexpr int kBlock = 256;              // threads per workgroup, one quad each
+constexpr int64_t kBlockElems = 4 * kBlock;
+constexpr int kStage2Blocks = 256;       // second reduction level
 
-// ---------------------------------------------------------------------------
-// Stage 1: acc = float(g) (first micro-batch) or acc = acc + float(g).
-template <bool FIRST>
-__global__ __launch_bounds__(kBlock) void grad_accumulate_kernel(float* __restrict__ acc,
-                                                                 const uint16_t* __restrict__ g,
-                                                                 int64_t n) {
-  const int64_t nvec = n >> 3;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const uint4* gv = reinterpret_cast<const uint4*>(g);
-  float4* av = reinterpret_cast<float4*>(acc);
-  for (int64_t base = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; base < nvec;
-       base += stride * kUnroll) {
-    uint4 gr[kUnroll];
-    float4 a0[kUnroll], a1[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t i = base + u * stride;
-      if (i < nvec) {
-        gr[u] = gv[i];
-        if (!FIRST) {
-          a0[u] = av[2 * i];
-          a1[u] = av[2 * i + 1];
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t i = base + u * stride;
-      if (i < nvec) {
-        float f[8];
-        unpack8(gr[u], f);
-        if (FIRST) {
-          av[2 * i] = make_float4(f[0], f[1], f[2], f[3]);
-          av[2 * i + 1] = make_float4(f[4], f[5], f[6], f[7]);
-        } else {
-          av[2 * i] = make_float4(a0[u].x + f[0], a0[u].y + f[1], a0[u].z + f[2], a0[u].w + f[3]);
-          av[2 * i + 1] =
-              make_float4(a1[u].x + f[4], a1[u].y + f[5], a1[u].z + f[6], a1[u].w + f[7]);
-        }
-      }
-    }
-  }
-  if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
-    const int64_t j = (nvec << 3) + threadIdx.x;
-    const float gf = __uint_as_float((uint32_t)g[j] << 16);
-    acc[j] = FIRST ? gf : acc[j] + gf;
-  }
+// Workgroups of a flat pass over n elements, rounded up to a multiple of 8 so
+// that the XCD remap below is a permutation.
+int64_t quad_blocks(int64_t n) {
+  int64_t g = (n + kBlockElems - 1) / kBlockElems;
+  if (g < 8) g = 8;
+  return (g + 7) / 8 * 8;
+}
+
+// Logical block of this workgroup: block b runs on XCD b % 8; XCD x gets the
+// contiguous logical range [x*G/8, (x+1)*G/8).
+__device__ __forceinline__ int64_t xcd_block() {
+  const int64_t b = blockIdx.x;
+  const int64_t g = gridDim.x;
+  return (b & 7) * (g >> 3) + (b >> 3);
+}
+
+// FP64 block sum (fixed order: shuffles in the wave, then waves in order).
+__device__ __forceinline__ double block_sum_f64(double s) {
+  __shared__ double lds[kBlock / kWave];
+  s = wave_sum_f64(s);
+  if ((threadIdx.x & (kWave - 1)) == 0) lds[threadIdx.x / kWave] = s;
+  __syncthreads();
+  return (lds[0] + lds[1]) + (lds[2] + lds[3]);
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2a: per-workgroup FP64 partial sums of acc^2.
+// Stage 1: acc = float(g) (first micro-batch) or acc = acc + float(g); with
+// SUMSQ also the block's FP64 sum of the new acc^2.
+template <bool FIRST, bool SUMSQ>
+__global__ __launch_bounds__(kBlock) void grad_accumulate_kernel(float* __restrict__ acc,
+                                                                 const uint16_t* __restrict__ g,
+                                                                 int64_t n,
+                                                                 double* __restrict__ partial) {
+  const int64_t lb = xcd_block();
+  const int64_t q = lb * kBlock + threadIdx.x;
+  const int64_t e0 = q * 4;
+  double s = 0.0;
+  if (e0 + 4 <= n) {
+    const uint2 gv = reinterpret_cast<const uint2*>(g)[q];
+    float4 r;
+    if (FIRST) {
+      r = make_float4(bf16_lo(gv.x), bf16_hi(gv.x), bf16_lo(gv.y), bf16_hi(gv.y));
+    } else {
+      r = reinterpret_cast<const float4*>(acc)[q];
+      r.x += bf16_lo(gv.x);
+      r.y += bf16_hi(gv.x);
+      r.z += bf16_lo(gv.y);
+      r.w += bf16_hi(gv.y);
+    }
+    reinterpret_cast<float4*>(acc)[q] = r;
+    if (SUMSQ) {
+      s = fma((double)r.x, (double)r.x, s);
+      s = fma((double)r.y, (double)r.y, s);
+      s = fma((double)r.z, (double)r.z, s);
+      s = fma((double)r.w, (double)r.w, s);
+    }
+  } else if (e0 < n) {
+    for (int64_t j = e0; j < n; ++j) {
+      const float gf = __uint_as_float((uint32_t)g[j] << 16);
+      const float r = FIRST ? gf : acc[j] + gf;
+      acc[j] = r;
+      if (SUMSQ) s = fma((double)r, (double)r, s);
+    }
+  }
+  if (SUMSQ) {
+    s = block_sum_f64(s);
+    if (threadIdx.x == 0) partial[lb] = s;
+  }
+}
+
+// Stage 2a (standalone): the same per-block partials from a read of acc.
 __global__ __launch_bounds__(kBlock) void sumsq_kernel(const float* __restrict__ acc, int64_t n,
                                                        double* __restrict__ partial) {
-  __shared__ double lds[kBlock / kWave];
-  const int64_t nvec = n >> 2;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const float4* av = reinterpret_cast<const float4*>(acc);
-  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-  for (int64_t base = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; base < nvec;
-       base += stride * 4) {
-    float4 a[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t i = base + u * stride;
-      a[u] = (i < nvec) ? av[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      s0 = fma((double)a[u].x, (double)a[u].x, s0);
-      s1 = fma((double)a[u].y, (double)a[u].y, s1);
-      s2 = fma((double)a[u].z, (double)a[u].z, s2);
-      s3 = fma((double)a[u].w, (double)a[u].w, s3);
-    }
+  const int64_t lb = xcd_block();
+  const int64_t q = lb * kBlock + threadIdx.x;
+  const int64_t e0 = q * 4;
+  double s = 0.0;
+  if (e0 + 4 <= n) {
+    const float4 r = reinterpret_cast<const float4*>(acc)[q];
+    s = fma((double)r.x, (double)r.x, s);
+    s = fma((double)r.y, (double)r.y, s);
+    s = fma((double)r.z, (double)r.z, s);
+    s = fma((double)r.w, (double)r.w, s);
+  } else if (e0 < n) {
+    for (int64_t j = e0; j < n; ++j) s = fma((double)acc[j], (double)acc[j], s);
   }
-  if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
-    const double t = (double)acc[(nvec << 2) + threadIdx.x];
-    s0 = fma(t, t, s0);
-  }
-  double s = wave_sum_f64((s0 + s1) + (s2 + s3));
-  if ((threadIdx.x & (kWave - 1)) == 0) lds[threadIdx.x / kWave] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double b = 0.0;
-    for (int w = 0; w < kBlock / kWave; ++w) b += lds[w];
-    partial[blockIdx.x] = b;
-  }
+  s = block_sum_f64(s);
+  if (threadIdx.x == 0) partial[lb] = s;
+}
+
+// Stage 2b: workgroup j adds partials [j*chunk, (j+1)*chunk) in a fixed order.
+__global__ __launch_bounds__(kBlock) void partial_reduce_kernel(const double* __restrict__ partial,
+                                                                int64_t parts, int64_t chunk,
+                                                                double* __restrict__ out) {
+  const int64_t lo = (int64_t)blockIdx.x * chunk;
+  int64_t hi = lo + chunk;
+  if (hi > parts) hi = parts;
+  double s = 0.0;
+  for (int64_t p = lo + threadIdx.x; p < hi; p += kBlock) s += partial[p];
+  s = block_sum_f64(s);
+  if (threadIdx.x == 0) out[blockIdx.x] = s;
 }
 
 struct NormState {
@@ -128,19 +149,13 @@ struct NormState {
   float pad[3];
 };
 
-// Stage 2b: one workgroup adds the partials in order, forms N and c.
-__global__ __launch_bounds__(kBlock) void norm_finalize_kernel(const double* __restrict__ partial,
-                                                               int parts, double max_norm,
+// Stage 2c: one workgroup adds the stage-2 sums in order, forms N and c.
+__global__ __launch_bounds__(kBlock) void norm_finalize_kernel(const double* __restrict__ part2,
+                                                               double max_norm,
                                                                NormState* __restrict__ state,
                                                                float* __restrict__ norm_out) {
-  __shared__ double lds[kBlock];
-  double s = 0.0;
-  for (int p = threadIdx.x; p < parts; p += kBlock) s += partial[p];
-  lds[threadIdx.x] = s;
-  __syncthreads();
+  const double t = block_sum_f64(part2[threadIdx.x]);
   if (threadIdx.x == 0) {
-    double t = 0.0;
-    for (int k = 0; k < kBlock; ++k) t += lds[k];
     const double nrm = sqrt(t);
     // NaN compares false and leaves c = 1; an infinite norm gives c = 0.
     const double c = (nrm > max_norm) ? max_norm / nrm : 1.0;
@@ -179,65 +194,76 @@ __global__ __launch_bounds__(kBlock) void adamw_kernel(float* __restrict__ maste
                                                        const NormState* __restrict__ state,
                                                        AdamConsts k) {
   const float c = state->clip;
-  const int64_t nvec = n >> 3;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const float4* av = reinterpret_cast<const float4*>(acc);
-  float4* pv = reinterpret_cast<float4*>(master);
-  float4* mv = reinterpret_cast<float4*>(exp_avg);
-  float4* vv = reinterpret_cast<float4*>(exp_avg_sq);
-  uint4* ov = reinterpret_cast<uint4*>(param);
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
-    float a[8], p[8], m[8], v[8];
-    *reinterpret_cast<float4*>(a) = av[2 * i];
-    *reinterpret_cast<float4*>(a + 4) = av[2 * i + 1];
-    *reinterpret_cast<float4*>(p) = pv[2 * i];
-    *reinterpret_cast<float4*>(p + 4) = pv[2 * i + 1];
-    *reinterpret_cast<float4*>(m) = mv[2 * i];
-    *reinterpret_cast<float4*>(m + 4) = mv[2 * i + 1];
-    *reinterpret_cast<float4*>(v) = vv[2 * i];
-    *reinterpret_cast<float4*>(v + 4) = vv[2 * i + 1];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) adam_one(a[e], c, p[e], m[e], v[e], k);
-    pv[2 * i] = *reinterpret_cast<float4*>(p);
-    pv[2 * i + 1] = *reinterpret_cast<float4*>(p + 4);
-    mv[2 * i] = *reinterpret_cast<float4*>(m);
-    mv[2 * i + 1] = *reinterpret_cast<float4*>(m + 4);
-    vv[2 * i] = *reinterpret_cast<float4*>(v);
-    vv[2 * i + 1] = *reinterpret_cast<float4*>(v + 4);
-    ov[i] = pack8(p);
-  }
-  if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
-    const int64_t j = (nvec << 3) + threadIdx.x;
-    float p = master[j], m = exp_avg[j], v = exp_avg_sq[j];
-    adam_one(acc[j], c, p, m, v, k);
-    master[j] = p;
-    exp_avg[j] = m;
-    exp_avg_sq[j] = v;
-    param[j] = (uint16_t)(pack2(p, 0.f) & 0xffffu);
+  const int64_t q = xcd_block() * kBlock + threadIdx.x;
+  const int64_t e0 = q * 4;
+  if (e0 + 4 <= n) {
+    const float4 a = reinterpret_cast<const float4*>(acc)[q];
+    float4 p = reinterpret_cast<const float4*>(master)[q];
+    float4 m = reinterpret_cast<const float4*>(exp_avg)[q];
+    float4 v = reinterpret_cast<const float4*>(exp_avg_sq)[q];
+    adam_one(a.x, c, p.x, m.x, v.x, k);
+    adam_one(a.y, c, p.y, m.y, v.y, k);
+    adam_one(a.z, c, p.z, m.z, v.z, k);
+    adam_one(a.w, c, p.w, m.w, v.w, k);
+    reinterpret_cast<float4*>(master)[q] = p;
+    reinterpret_cast<float4*>(exp_avg)[q] = m;
+    reinterpret_cast<float4*>(exp_avg_sq)[q] = v;
+    reinterpret_cast<uint2*>(param)[q] = make_uint2(pack2(p.x, p.y), pack2(p.z, p.w));
+  } else if (e0 < n) {
+    for (int64_t j = e0; j < n; ++j) {
+      float p = master[j], m = exp_avg[j], v = exp_avg_sq[j];
+      adam_one(acc[j], c, p, m, v, k);
+      master[j] = p;
+      exp_avg[j] = m;
+      exp_avg_sq[j] = v;
+      param[j] = (uint16_t)(pack2(p, 0.f) & 0xffffu);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-int stream_grid(int64_t nvec, int blocks_per_cu) {
-  const int64_t cap = (int64_t)device_cu_count() * blocks_per_cu;
-  int64_t need = (nvec + kBlock - 1) / kBlock;
-  if (need < 1) need = 1;
-  return (int)(need < cap ? need : cap);
-}
+// Workspace: [partials: quad_blocks(n) doubles][stage 2: 256 doubles][NormState],
+// each part 256-byte aligned.
+struct WorkspaceLayout {
+  size_t partial_off, stage2_off, state_off, total;
+};
 
-int norm_parts(int64_t n) {
-  const int64_t nvec = n >> 2;
-  const int64_t cap = (int64_t)device_cu_count() * kNormBlocksPerCu;
-  int64_t need = (nvec + kBlock - 1) / kBlock;
-  if (need < 1) need = 1;
-  return (int)(need < cap ? need : cap);
-}
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-size_t adamw_workspace_bytes(int64_t n) {
-  return (size_t)norm_parts(n) * sizeof(double) + sizeof(NormState) + 256;
+WorkspaceLayout workspace_layout(int64_t n) {
+  WorkspaceLayout w;
+  w.partial_off = 0;
+  w.stage2_off = align256((size_t)quad_blocks(n) * sizeof(double));
+  w.state_off = w.stage2_off + align256(kStage2Blocks * sizeof(double));
+  w.total = w.state_off + align256(sizeof(NormState));
+  return w;
 }
 
 bool finite_nonneg(double x) { return std::isfinite(x) && x >= 0.0; }
+
+bloom_status launch_accumulate(float* acc, const bloom_bf16* grad, int64_t n, int32_t first,
+                               double* partial, hipStream_t stream) {
+  const dim3 grid((unsigned)quad_blocks(n));
+  if (partial == nullptr) {
+    if (first)
+      hipLaunchKernelGGL((grad_accumulate_kernel<true, false>), grid, dim3(kBlock), 0, stream, acc,
+                         grad, n, partial);
+    else
+      hipLaunchKernelGGL((grad_accumulate_kernel<false, false>), grid, dim3(kBlock), 0, stream,
+                         acc, grad, n, partial);
+  } else {
+    if (first)
+      hipLaunchKernelGGL((grad_accumulate_kernel<true, true>), grid, dim3(kBlock), 0, stream, acc,
+                         grad, n, partial);
+    else
+      hipLaunchKernelGGL((grad_accumulate_kernel<false, true>), grid, dim3(kBlock), 0, stream, acc,
+                         grad, n, partial);
+  }
+  return launch_status("bloom_bf16_grad_accumulate");
+}
+
+// Largest n: quad_blocks(n) must fit a 32-bit grid.
+constexpr int64_t kMaxElems = (int64_t)0x7ffffff0 * kBlockElems;
 
 }  // namespace
 }  // namespace bloom
@@ -248,23 +274,34 @@ extern "C" bloom_status bloom_bf16_grad_accumulate(float* grad_acc, const bloom_
                                                    int64_t n, int32_t first_microbatch,
                                                    hipStream_t stream) {
   clear_error();
-  BLOOM_REQUIRE(n >= 0, BLOOM_ERR_SHAPE, "n = %lld is negative", (long long)n);
+  BLOOM_REQUIRE(n >= 0 && n <= kMaxElems, BLOOM_ERR_SHAPE, "n = %lld out of range", (long long)n);
   if (n == 0) return BLOOM_OK;
   BLOOM_REQUIRE_PTR(grad_acc);
   BLOOM_REQUIRE_PTR(grad);
-  const int grid = stream_grid(n >> 3, 8);
-  if (first_microbatch)
-    hipLaunchKernelGGL(grad_accumulate_kernel<true>, dim3(grid), dim3(kBlock), 0, stream, grad_acc,
-                       grad, n);
-  else
-    hipLaunchKernelGGL(grad_accumulate_kernel<false>, dim3(grid), dim3(kBlock), 0, stream,
-                       grad_acc, grad, n);
-  return launch_status("bloom_bf16_grad_accumulate");
+  return launch_accumulate(grad_acc, grad, n, first_microbatch, nullptr, stream);
 }
 
 extern "C" size_t bloom_bf16_adamw_workspace_size(int64_t n) {
-  if (n < 0) return 0;
-  return adamw_workspace_bytes(n);
+  if (n < 0 || n > kMaxElems) return 0;
+  return workspace_layout(n).total;
+}
+
+extern "C" bloom_status bloom_bf16_grad_accumulate_sumsq(float* grad_acc, const bloom_bf16* grad,
+                                                         int64_t n, int32_t first_microbatch,
+                                                         void* workspace, size_t workspace_bytes,
+                                                         hipStream_t stream) {
+  clear_error();
+  BLOOM_REQUIRE(n >= 0 && n <= kMaxElems, BLOOM_ERR_SHAPE, "n = %lld out of range", (long long)n);
+  if (n == 0) return BLOOM_OK;
+  BLOOM_REQUIRE_PTR(grad_acc);
+  BLOOM_REQUIRE_PTR(grad);
+  BLOOM_REQUIRE(workspace != nullptr, BLOOM_ERR_WORKSPACE, "workspace is NULL");
+  BLOOM_REQUIRE(aligned16(workspace), BLOOM_ERR_ALIGN, "workspace is not 16-byte aligned");
+  const WorkspaceLayout w = workspace_layout(n);
+  BLOOM_REQUIRE(workspace_bytes >= w.total, BLOOM_ERR_WORKSPACE,
+                "workspace has %zu bytes, needs %zu", workspace_bytes, w.total);
+  double* partial = reinterpret_cast<double*>(static_cast<char*>(workspace) + w.partial_off);
+  return launch_accumulate(grad_acc, grad, n, first_microbatch, partial, stream);
 }
 
 extern "C" bloom_status bloom_bf16_adamw_step(float* master, float* exp_avg, float* exp_avg_sq,
@@ -273,7 +310,7 @@ extern "C" bloom_status bloom_bf16_adamw_step(float* master, float* exp_avg, flo
                                               float* grad_norm_out, void* workspace,
                                               size_t workspace_bytes, hipStream_t stream) {
   clear_error();
-  BLOOM_REQUIRE(n >= 0, BLOOM_ERR_SHAPE, "n = %lld is negative", (long long)n);
+  BLOOM_REQUIRE(n >= 0 && n <= kMaxElems, BLOOM_ERR_SHAPE, "n = %lld out of range", (long long)n);
   BLOOM_REQUIRE(hp != nullptr, BLOOM_ERR_NULL, "hp is NULL");
   BLOOM_REQUIRE(finite_nonneg(hp->lr), BLOOM_ERR_HPARAM, "lr must be finite and >= 0");
   BLOOM_REQUIRE(hp->beta1 >= 0.0 && hp->beta1 < 1.0, BLOOM_ERR_HPARAM, "beta1 must be in [0, 1)");
@@ -284,6 +321,9 @@ extern "C" bloom_status bloom_bf16_adamw_step(float* master, float* exp_avg, flo
                 "weight_decay must be finite and >= 0");
   BLOOM_REQUIRE(hp->max_grad_norm > 0.0, BLOOM_ERR_HPARAM, "max_grad_norm must be > 0");
   BLOOM_REQUIRE(hp->step >= 1, BLOOM_ERR_HPARAM, "step must be >= 1");
+  BLOOM_REQUIRE(hp->sumsq_in_workspace == 0 || hp->sumsq_in_workspace == 1, BLOOM_ERR_HPARAM,
+                "sumsq_in_workspace must be 0 or 1");
+  BLOOM_REQUIRE(hp->reserved == 0, BLOOM_ERR_HPARAM, "reserved must be 0");
   if (n == 0) return BLOOM_OK;
   BLOOM_REQUIRE_PTR(master);
   BLOOM_REQUIRE_PTR(exp_avg);
@@ -292,9 +332,9 @@ extern "C" bloom_status bloom_bf16_adamw_step(float* master, float* exp_avg, flo
   BLOOM_REQUIRE_PTR(grad_acc);
   BLOOM_REQUIRE(workspace != nullptr, BLOOM_ERR_WORKSPACE, "workspace is NULL");
   BLOOM_REQUIRE(aligned16(workspace), BLOOM_ERR_ALIGN, "workspace is not 16-byte aligned");
-  const size_t need = adamw_workspace_bytes(n);
-  BLOOM_REQUIRE(workspace_bytes >= need, BLOOM_ERR_WORKSPACE,
-                "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  const WorkspaceLayout w = workspace_layout(n);
+  BLOOM_REQUIRE(workspace_bytes >= w.total, BLOOM_ERR_WORKSPACE,
+                "workspace has %zu bytes, needs %zu", workspace_bytes, w.total);
   BLOOM_REQUIRE(grad_norm_out == nullptr || (reinterpret_cast<uintptr_t>(grad_norm_out) & 3) == 0,
                 BLOOM_ERR_ALIGN, "grad_norm_out is not 4-byte aligned");
 
@@ -311,17 +351,23 @@ extern "C" bloom_status bloom_bf16_adamw_step(float* master, float* exp_avg, flo
   k.eps = (float)hp->eps;
   k.lr_wd = (float)(hp->lr * hp->weight_decay);
 
-  const int parts = norm_parts(n);
-  double* partial = static_cast<double*>(workspace);
-  NormState* state = reinterpret_cast<NormState*>(
-      static_cast<char*>(workspace) + ((size_t)parts * sizeof(double) + 255) / 256 * 256);
-  hipLaunchKernelGGL(sumsq_kernel, dim3(parts), dim3(kBlock), 0, stream, grad_acc, n, partial);
-  if (bloom_status st = launch_status("bloom_bf16_adamw_step: norm")) return st;
-  hipLaunchKernelGGL(norm_finalize_kernel, dim3(1), dim3(kBlock), 0, stream, partial, parts,
+  char* ws = static_cast<char*>(workspace);
+  double* partial = reinterpret_cast<double*>(ws + w.partial_off);
+  double* stage2 = reinterpret_cast<double*>(ws + w.stage2_off);
+  NormState* state = reinterpret_cast<NormState*>(ws + w.state_off);
+  const int64_t parts = quad_blocks(n);
+  if (!hp->sumsq_in_workspace) {
+    hipLaunchKernelGGL(sumsq_kernel, dim3((unsigned)parts), dim3(kBlock), 0, stream, grad_acc, n,
+                       partial);
+    if (bloom_status st = launch_status("bloom_bf16_adamw_step: norm")) return st;
+  }
+  const int64_t chunk = (parts + kStage2Blocks - 1) / kStage2Blocks;
+  hipLaunchKernelGGL(partial_reduce_kernel, dim3(kStage2Blocks), dim3(kBlock), 0, stream, partial,
+                     parts, chunk, stage2);
+  hipLaunchKernelGGL(norm_finalize_kernel, dim3(1), dim3(kBlock), 0, stream, stage2,
                      hp->max_grad_norm, state, grad_norm_out);
   if (bloom_status st = launch_status("bloom_bf16_adamw_step: clip")) return st;
-  const int grid = stream_grid(n >> 3, 8);
-  hipLaunchKernelGGL(adamw_kernel, dim3(grid), dim3(kBlock), 0, stream, master, exp_avg,
+  hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)parts), dim3(kBlock), 0, stream, master, exp_avg,
                      exp_avg_sq, param_bf16, grad_acc, n, state, k);
   return launch_status("bloom_bf16_adamw_step: update");
 }

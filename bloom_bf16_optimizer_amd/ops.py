@@ -152,13 +152,23 @@ def bloom_bf16_grad_accumulate(grad_acc, grad, first_microbatch: bool) -> None:
         _stream()))
 
 
+def bloom_bf16_grad_accumulate_sumsq(grad_acc, grad, first_microbatch: bool, workspace) -> None:
+    if grad_acc.numel() != grad.numel():
+        raise ValueError("grad_acc and grad must have the same number of elements")
+    wsb = workspace.numel() * workspace.element_size()
+    lib = _lib.load()
+    check("bloom_bf16_grad_accumulate_sumsq", lib.bloom_bf16_grad_accumulate_sumsq(
+        _ptr(grad_acc, F32, "grad_acc"), _ptr(grad, BF16, "grad"), grad.numel(), int(bool(first_microbatch)),
+        _ptr(workspace, workspace.dtype, "workspace"), wsb, _stream()))
+
+
 def bloom_bf16_adamw_workspace_size(n: int) -> int:
     return _lib.load().bloom_bf16_adamw_workspace_size(n)
 
 
 def adamw_hparams(lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
-                  max_grad_norm: float, step: int) -> AdamWHParams:
-    return AdamWHParams(lr, beta1, beta2, eps, weight_decay, max_grad_norm, step)
+                  max_grad_norm: float, step: int, sumsq_in_workspace: bool = False) -> AdamWHParams:
+    return AdamWHParams(lr, beta1, beta2, eps, weight_decay, max_grad_norm, step, int(bool(sumsq_in_workspace)), 0)
 
 
 def bloom_bf16_adamw_step(master, exp_avg, exp_avg_sq, param_bf16, grad_acc, hp: AdamWHParams,

@@ -183,7 +183,23 @@ typedef struct {
   double weight_decay;  /* >= 0; [3d] 3.3 and [mini] 3 use 0.01 */
   double max_grad_norm; /* > 0; [3d] 4.3 and [mini] 3 use 1.0 */
   int64_t step;         /* t >= 1 of this update (bias correction 1 - beta^t) */
+  int32_t sumsq_in_workspace; /* 1: the workspace already holds the norm's partial
+                                 sums, written by bloom_bf16_grad_accumulate_sumsq
+                                 for this n and grad_acc, and the step skips its own
+                                 read of grad_acc for the norm; 0: the step computes them */
+  int32_t reserved;     /* must be 0 */
 } bloom_adamw_hparams;
+
+/* Stage 1 for the last micro-batch: the same accumulation as
+ * bloom_bf16_grad_accumulate, and in the same pass the FP64 partial sums of
+ * grad_acc^2 that the norm of bloom_bf16_adamw_step needs, written into
+ * `workspace` (sized by bloom_bf16_adamw_workspace_size(n)).  Pass that
+ * workspace to bloom_bf16_adamw_step with hp->sumsq_in_workspace = 1 and leave
+ * grad_acc unchanged in between; the step then reads grad_acc once instead of
+ * twice.  The norm is bit-identical to the one the step computes by itself. */
+bloom_status bloom_bf16_grad_accumulate_sumsq(float* grad_acc, const bloom_bf16* grad, int64_t n,
+                                              int32_t first_microbatch, void* workspace,
+                                              size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace bloom_bf16_adamw_step needs (norm partials and the
  * clip coefficient). */

@@ -124,6 +124,10 @@ def gen(shape, seed: int, stream: int, sigma: float, offset: float = 0.0, dtype=
 
 
 def sample_rows(total: int, k: int, seed: int, must=()) -> np.ndarray:
+    """k distinct random indices in [0, total) plus the `must` ones (all checked in range)."""
+    must = [int(m) for m in must]
+    if any(m < 0 or m >= total for m in must):
+        raise ValueError(f"sample index out of range [0, {total})")
     rng = np.random.default_rng(seed)
     pick = rng.choice(total, size=min(k, total), replace=False)
     return np.unique(np.concatenate([pick, np.asarray(list(must), dtype=np.int64)])).astype(np.int64)

@@ -50,7 +50,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.bloom_abi_version() == 1
+    assert lib.bloom_abi_version() == 2
     assert lib.bloom_status_string(0) == b"ok"
     assert lib.bloom_status_string(4) == b"workspace too small"
     assert lib.bloom_status_string(99) == b"unknown status"
@@ -125,14 +125,15 @@ def test_gelu_validation(lib):
 
 def test_optimizer_validation(lib):
     p = FAKE
-    hp = _lib.AdamWHParams(6e-5, 0.9, 0.999, 1e-8, 0.01, 1.0, 1)
+    hp = _lib.AdamWHParams(6e-5, 0.9, 0.999, 1e-8, 0.01, 1.0, 1, 0, 0)
     ws = lib.bloom_bf16_adamw_workspace_size(1000)
     assert ws > 0
     step = lib.bloom_bf16_adamw_step
     assert step(p, p, p, p, p, 1000, None, None, p, ws, None) == NULL
     for field, bad in [("lr", -1.0), ("beta1", 1.0), ("beta2", -0.1), ("eps", 0.0),
-                       ("weight_decay", float("nan")), ("max_grad_norm", 0.0), ("step", 0)]:
-        h = _lib.AdamWHParams(6e-5, 0.9, 0.999, 1e-8, 0.01, 1.0, 1)
+                       ("weight_decay", float("nan")), ("max_grad_norm", 0.0), ("step", 0),
+                       ("sumsq_in_workspace", 2), ("reserved", 1)]:
+        h = _lib.AdamWHParams(6e-5, 0.9, 0.999, 1e-8, 0.01, 1.0, 1, 0, 0)
         setattr(h, field, bad)
         assert step(p, p, p, p, p, 1000, ctypes.byref(h), None, p, ws, None) == HPARAM, field
     assert step(p, p, p, p, p, 1000, ctypes.byref(hp), None, p, ws - 8, None) == WORKSPACE
@@ -140,6 +141,13 @@ def test_optimizer_validation(lib):
     assert step(p, p, p, p, p, 1000, ctypes.byref(hp), p + 2, p, ws, None) == ALIGN
     assert step(p, p, p, p, p, 0, ctypes.byref(hp), None, None, 0, None) == OK
     assert step(p, p, p, p, p, -5, ctypes.byref(hp), None, p, ws, None) == SHAPE
+    fused = lib.bloom_bf16_grad_accumulate_sumsq
+    assert fused(p, p, 1000, 0, None, 0, None) == WORKSPACE
+    assert fused(p, p, 1000, 0, p, ws - 8, None) == WORKSPACE
+    assert fused(p, p, 1000, 0, p + 8, ws, None) == ALIGN
+    assert fused(p, p, 0, 0, None, 0, None) == OK
+    # the workspace holds one FP64 partial per 1024-element workgroup (grid rounded to 8)
+    assert lib.bloom_bf16_adamw_workspace_size(3_670_000_000) >= 8 * (3_670_000_000 // 1024)
     acc = lib.bloom_bf16_grad_accumulate
     assert acc(p, p, -1, 1, None) == SHAPE
     assert acc(p, None, 10, 1, None) == NULL

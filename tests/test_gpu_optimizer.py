@@ -18,17 +18,23 @@ HP = dict(lr=W.LR, beta1=W.BETA1, beta2=W.BETA2, eps=W.ADAM_EPS, weight_decay=W.
           max_grad_norm=W.MAX_GRAD_NORM)
 
 
-def _hp(step, **over):
+def _hp(step, sumsq_in_workspace=False, **over):
     d = dict(HP)
     d.update(over)
-    return ops.adamw_hparams(d["lr"], d["beta1"], d["beta2"], d["eps"], d["weight_decay"], d["max_grad_norm"], step)
+    return ops.adamw_hparams(d["lr"], d["beta1"], d["beta2"], d["eps"], d["weight_decay"], d["max_grad_norm"], step,
+                             sumsq_in_workspace)
 
 
-def _step_gpu(master, m, v, acc, hp):
+def _workspace(n):
+    return torch.empty(ops.bloom_bf16_adamw_workspace_size(n), dtype=torch.uint8, device="cuda")
+
+
+def _step_gpu(master, m, v, acc, hp, ws=None):
     n = master.numel()
     param = torch.empty(n, dtype=torch.bfloat16, device="cuda")
     norm = torch.empty(1, dtype=torch.float32, device="cuda")
-    ws = torch.empty(ops.bloom_bf16_adamw_workspace_size(n), dtype=torch.uint8, device="cuda")
+    if ws is None:
+        ws = _workspace(n)
     ops.bloom_bf16_adamw_step(master, m, v, param, acc, hp, norm, ws)
     torch.cuda.synchronize()
     return param, float(norm.item())
@@ -58,12 +64,17 @@ def _compare_step(tag, gpu_master, gpu_m, gpu_v, gpu_param, f64, terms, ref_para
     assert np.all(np.abs(a[fin] - b[fin]) <= 1), f"{tag} param vs oracle"
 
 
-def _accumulate_gpu(n, seed, microbatches, start_stream=W.S_OPT_GRAD0 + 1):
+def _accumulate_gpu(n, seed, microbatches, start_stream=W.S_OPT_GRAD0 + 1, ws=None):
+    """Accumulates the micro-batch gradients; with a workspace the last call is
+    the fused accumulate + norm-partials entry point."""
     acc = torch.empty(n, dtype=torch.float32, device="cuda")
     g = torch.empty(n, dtype=torch.bfloat16, device="cuda")
     for k in range(microbatches):
         sdev.fill_(g, seed, start_stream + k, W.GRAD_SIGMA)
-        ops.bloom_bf16_grad_accumulate(acc, g, first_microbatch=(k == 0))
+        if ws is not None and k == microbatches - 1:
+            ops.bloom_bf16_grad_accumulate_sumsq(acc, g, k == 0, ws)
+        else:
+            ops.bloom_bf16_grad_accumulate(acc, g, first_microbatch=(k == 0))
     torch.cuda.synchronize()
     return acc
 
@@ -100,6 +111,28 @@ def test_step_small(n, mb, step, zero_moments):
     (rp, rm, rv, rpb), f64, terms, rnorm = _oracle_step(p, m, v, ref_acc, step)
     assert abs(norm - rnorm) <= 1e-6 * rnorm, (norm, rnorm)
     _compare_step(f"n={n}", tp.cpu().numpy(), tm.cpu().numpy(), tv.cpu().numpy(), host_bf16(param), f64, terms, rpb)
+
+
+@pytest.mark.parametrize("n,mb", [(1_000_003, 3), (4096, 1), (5, 2), (3_000_000, 32)])
+def test_fused_norm_partials_match_standalone(n, mb):
+    """The last micro-batch's fused accumulate + norm partials, then the step
+    with sumsq_in_workspace = 1, gives the same bits as the unfused path."""
+    require_gpu()
+    seed = 6
+    outs = []
+    for fused in (False, True):
+        tp = gen((n,), seed, W.S_OPT_PARAM, W.PARAM_SIGMA, dtype=torch.float32)[0]
+        tm = gen((n,), seed, W.S_OPT_M, W.M_SIGMA, dtype=torch.float32)[0]
+        tv = gen((n,), seed, W.S_OPT_V, W.V_SIGMA, dtype=torch.float32, absolute=True)[0]
+        ws = _workspace(n)
+        acc = _accumulate_gpu(n, seed, mb, ws=ws if fused else None)
+        param, norm = _step_gpu(tp, tm, tv, acc, _hp(4, sumsq_in_workspace=fused), ws=ws)
+        outs.append([acc.cpu().numpy(), tp.cpu().numpy(), tm.cpu().numpy(), tv.cpu().numpy(),
+                     host_bf16(param), np.array([norm], dtype=np.float32)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    ref = oopt.global_norm(_accumulate_oracle(np.arange(n, dtype=np.uint64), seed, mb))
+    assert abs(float(outs[1][5][0]) - ref) <= 1e-6 * ref
 
 
 def test_two_steps_and_checkpoint_round_trip():
@@ -223,8 +256,9 @@ def test_shard_optimizer_full_size():
     require_gpu()
     wl = W.OPTIMIZER
     n, mb = wl.opt.n, wl.opt.microbatches
-    tacc = _accumulate_gpu(n, wl.seed, mb)
-    idx = sample_rows(n, 300_000, 43, must=list(range(8)) + list(range(n - 8, n)) + [2 ** 32, 2 ** 31])
+    ws = _workspace(n)
+    tacc = _accumulate_gpu(n, wl.seed, mb, ws=ws)   # last micro-batch fused with the norm partials
+    idx = sample_rows(n, 300_000, 43, must=list(range(8)) + list(range(n - 8, n)) + [2 ** 31 - 1, 2 ** 31, 3 * 2 ** 30])
     ti = torch.from_numpy(idx).cuda()
     acc_s = tacc[ti].cpu().numpy()
     ref_acc = _accumulate_oracle(idx.astype(np.uint64), wl.seed, mb)
@@ -238,7 +272,7 @@ def test_shard_optimizer_full_size():
     tp = gen((n,), wl.seed, W.S_OPT_PARAM, W.PARAM_SIGMA, dtype=torch.float32)[0]
     tm = torch.zeros(n, dtype=torch.float32, device="cuda")
     tv = torch.zeros(n, dtype=torch.float32, device="cuda")
-    param, norm = _step_gpu(tp, tm, tv, tacc, _hp(1))
+    param, norm = _step_gpu(tp, tm, tv, tacc, _hp(1, sumsq_in_workspace=True), ws=ws)
     assert abs(norm - rnorm) <= 1e-6 * rnorm, (norm, rnorm)
     assert norm > 300.0  # clipping active (expected about 342.7)
     p = synth.values(wl.seed, W.S_OPT_PARAM, idx, W.PARAM_SIGMA)
