@@ -18,7 +18,11 @@ Prints one JSON line.  `value` is the whole step's algorithmic HBM throughput
 (sum of each kernel's algorithmic bytes / step time, GB/s); per-kernel
 algorithmic GB/s, the fraction of the 8 TB/s HBM peak and the AdamW step time
 are reported beside it, with a roofline entry for the dominant kernel (the
-accumulation) and the CPU oracle timed on a bounded sample.
+accumulation) and the CPU oracle timed on a bounded sample.  The optimizer
+kernels are timed with events around each launch inside the timed steps; the
+fused kernels (tens of microseconds, where an event pair adds a few) are also
+timed after the steps in a sweep of back-to-back launches over rotating cold
+input sets, and that figure is their per-kernel number.
 """
 
 from __future__ import annotations
@@ -100,6 +104,15 @@ def run_gpu(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counter values
+        # against 1 GiB give the scale for the counter-measured traffic.
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     X = W.SHARD
     O = W.OPTIMIZER
     n = O.opt.n if args.n is None else args.n
@@ -109,50 +122,71 @@ def run_gpu(args):
     grows, gcols = X.gelu.rows, X.gelu.cols
     bf, f32 = torch.bfloat16, torch.float32
     seed = X.seed
+    scale = X.softmax.scale
 
-    def fill(shape, stream, sigma, offset=0.0, dtype=bf):
+    def fill(shape, stream, sigma, offset=0.0, dtype=bf, s=0):
         t = torch.empty(shape, dtype=dtype, device=dev)
-        sdev.fill_(t, seed, stream, sigma, offset)
+        sdev.fill_(t, seed + 1000 * s, stream, sigma, offset)
         return t
 
-    log(f"bench: allocating the shard workload (n = {n:,}, {GRAD_BUFFERS} gradient buffers)")
-    # fused-kernel tensors; every kernel has its own inputs
-    ln_x = fill((rows, hid), W.S_LN_X, 1.0)
     ln_g = fill((hid,), W.S_LN_GAMMA, 0.02, 1.0)
     ln_b = fill((hid,), W.S_LN_BETA, 0.02)
-    ln_y = torch.empty_like(ln_x)
-    ln_mean = torch.empty(rows, dtype=f32, device=dev)
-    ln_rstd = torch.empty_like(ln_mean)
-    ln_x2 = fill((rows, hid), 50, 1.0)
-    ln_dy = fill((rows, hid), W.S_LN_DY, 1.0)
-    ln_dx = torch.empty_like(ln_x)
-    ln_dg = torch.empty(hid, dtype=bf, device=dev)
-    ln_db = torch.empty_like(ln_dg)
-    ln_ws = torch.empty(ops.bloom_layernorm_bwd_workspace_size(rows, hid), dtype=torch.uint8, device=dev)
-    ln_mean2 = torch.empty_like(ln_mean)
-    ln_rstd2 = torch.empty_like(ln_mean)
-    ops.bloom_layernorm_fwd(ln_x2, ln_g, ln_b, ln_dx, ln_mean2, ln_rstd2, W.LN_EPS)  # saved stats for the bwd
-
-    scale = X.softmax.scale
-    sm_s = fill((smb, smh, sms, sms), W.S_SM_SCORES, 1.0)
-    sm_p = torch.empty_like(sm_s)
-    sm_s2 = fill((smb, smh, sms, sms), 51, 1.0)
-    sm_y = torch.empty_like(sm_s)
-    ops.bloom_alibi_softmax_fwd(sm_s2, sm_y, X.softmax.head_offset, X.softmax.total_heads, scale)
-    del sm_s2
-    sm_dy = fill((smb, smh, sms, sms), W.S_SM_DPROBS, 1.0)
-    sm_ds = torch.empty_like(sm_s)
-
-    ge_x = fill((grows, gcols), W.S_GELU_X, 1.0)
     ge_b = fill((gcols,), W.S_GELU_BIAS, 0.02)
-    ge_y = torch.empty_like(ge_x)
-    ge_x2 = fill((grows, gcols), 52, 1.0)
-    ge_dy = fill((grows, gcols), W.S_GELU_DY, 1.0)
-    ge_dx = torch.empty_like(ge_x)
-    ge_db = torch.empty(gcols, dtype=bf, device=dev)
-    ge_ws = torch.empty(ops.bloom_bias_gelu_bwd_workspace_size(grows, gcols), dtype=torch.uint8, device=dev)
 
-    # optimizer shard
+    # Each fused kernel gets its own input set(s): set 0 runs in the step,
+    # sets 0..S-1 rotate in the per-kernel sweep so every launch reads cold data.
+    def ln_fwd_set(s):
+        x = fill((rows, hid), W.S_LN_X, 1.0, s=s)
+        y = torch.empty_like(x)
+        m = torch.empty(rows, dtype=f32, device=dev)
+        r = torch.empty_like(m)
+        return lambda: ops.bloom_layernorm_fwd(x, ln_g, ln_b, y, m, r, W.LN_EPS)
+
+    def ln_bwd_set(s):
+        x = fill((rows, hid), 50, 1.0, s=s)
+        dy = fill((rows, hid), W.S_LN_DY, 1.0, s=s)
+        dx = torch.empty_like(x)
+        m = torch.empty(rows, dtype=f32, device=dev)
+        r = torch.empty_like(m)
+        ops.bloom_layernorm_fwd(x, ln_g, ln_b, dx, m, r, W.LN_EPS)   # saved statistics for the backward
+        dg = torch.empty(hid, dtype=bf, device=dev)
+        db = torch.empty_like(dg)
+        ws = torch.empty(ops.bloom_layernorm_bwd_workspace_size(rows, hid), dtype=torch.uint8, device=dev)
+        return lambda: ops.bloom_layernorm_bwd(dy, x, ln_g, m, r, dx, dg, db, ws)
+
+    def sm_fwd_set(s):
+        sc = fill((smb, smh, sms, sms), W.S_SM_SCORES, 1.0, s=s)
+        p = torch.empty_like(sc)
+        return lambda: ops.bloom_alibi_softmax_fwd(sc, p, X.softmax.head_offset, X.softmax.total_heads, scale)
+
+    def sm_bwd_set(s):
+        sc = fill((smb, smh, sms, sms), 51, 1.0, s=s)
+        y = torch.empty_like(sc)
+        ops.bloom_alibi_softmax_fwd(sc, y, X.softmax.head_offset, X.softmax.total_heads, scale)
+        del sc
+        dy = fill((smb, smh, sms, sms), W.S_SM_DPROBS, 1.0, s=s)
+        ds = torch.empty_like(y)
+        return lambda: ops.bloom_alibi_softmax_bwd(y, dy, ds, scale)
+
+    def ge_fwd_set(s):
+        x = fill((grows, gcols), W.S_GELU_X, 1.0, s=s)
+        y = torch.empty_like(x)
+        return lambda: ops.bloom_bias_gelu_fwd(x, ge_b, y)
+
+    def ge_bwd_set(s):
+        x = fill((grows, gcols), 52, 1.0, s=s)
+        dy = fill((grows, gcols), W.S_GELU_DY, 1.0, s=s)
+        dx = torch.empty_like(x)
+        db = torch.empty(gcols, dtype=bf, device=dev)
+        ws = torch.empty(ops.bloom_bias_gelu_bwd_workspace_size(grows, gcols), dtype=torch.uint8, device=dev)
+        return lambda: ops.bloom_bias_gelu_bwd(dy, x, ge_b, dx, db, ws)
+
+    fused = [("layernorm_fwd", ln_fwd_set, 4), ("alibi_softmax_fwd", sm_fwd_set, 2),
+             ("bias_gelu_fwd", ge_fwd_set, 4), ("bias_gelu_bwd", ge_bwd_set, 4),
+             ("alibi_softmax_bwd", sm_bwd_set, 2), ("layernorm_bwd", ln_bwd_set, 4)]
+    step_fused = [(name, make(0)) for name, make, _ in fused]
+
+    log(f"bench: allocating the shard workload (n = {n:,}, {GRAD_BUFFERS} gradient buffers)")
     master = fill((n,), W.S_OPT_PARAM, W.PARAM_SIGMA, dtype=f32)
     exp_avg = torch.zeros(n, dtype=f32, device=dev)
     exp_avg_sq = torch.zeros(n, dtype=f32, device=dev)
@@ -164,8 +198,8 @@ def run_gpu(args):
     torch.cuda.synchronize()
     log(f"bench: resident {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
 
-    names = ["layernorm_fwd", "alibi_softmax_fwd", "bias_gelu_fwd", "bias_gelu_bwd", "alibi_softmax_bwd",
-             "layernorm_bwd", "grad_accumulate_first", "grad_accumulate", "grad_accumulate_last", "adamw_step"]
+    names = [name for name, _ in step_fused] + ["grad_accumulate_first", "grad_accumulate", "grad_accumulate_last",
+                                                "adamw_step"]
     ev = {k: [] for k in names}
 
     def timed(name, fn, record):
@@ -180,15 +214,8 @@ def run_gpu(args):
             fn()
 
     def step(t, record):
-        timed("layernorm_fwd", lambda: ops.bloom_layernorm_fwd(ln_x, ln_g, ln_b, ln_y, ln_mean, ln_rstd, W.LN_EPS),
-              record)
-        timed("alibi_softmax_fwd", lambda: ops.bloom_alibi_softmax_fwd(
-            sm_s, sm_p, X.softmax.head_offset, X.softmax.total_heads, scale), record)
-        timed("bias_gelu_fwd", lambda: ops.bloom_bias_gelu_fwd(ge_x, ge_b, ge_y), record)
-        timed("bias_gelu_bwd", lambda: ops.bloom_bias_gelu_bwd(ge_dy, ge_x2, ge_b, ge_dx, ge_db, ge_ws), record)
-        timed("alibi_softmax_bwd", lambda: ops.bloom_alibi_softmax_bwd(sm_y, sm_dy, sm_ds, scale), record)
-        timed("layernorm_bwd", lambda: ops.bloom_layernorm_bwd(ln_dy, ln_x2, ln_g, ln_mean2, ln_rstd2, ln_dx,
-                                                               ln_dg, ln_db, ln_ws), record)
+        for name, fn in step_fused:
+            timed(name, fn, record)
         for k in range(mb):
             g = grads[k % GRAD_BUFFERS]
             if k == mb - 1:   # the last micro-batch also writes the norm's partial sums
@@ -215,13 +242,33 @@ def run_gpu(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    per = {}
+    in_step = {}
     for k in names:
         ts = [a.elapsed_time(b) for a, b in ev[k]]
-        per[k] = sum(ts) / len(ts)
+        in_step[k] = sum(ts) / len(ts)
     log(f"bench: {ms_step:.2f} ms/step; grad norm {norm.item():.4f}")
+
+    # Per-kernel sweep of the fused kernels: R back-to-back launches rotating
+    # over S cold input sets between one pair of events, so the per-launch
+    # event overhead (a few microseconds) is amortised.
+    sweep = {}
+    reps = 24
+    for name, make, sets in ([] if args.no_sweep else fused):
+        fns = [step_fused[[nm for nm, _ in step_fused].index(name)][1]] + [make(s) for s in range(1, sets)]
+        for fn in fns:
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for r in range(reps):
+            fns[r % sets]()
+        b.record()
+        b.synchronize()
+        sweep[name] = a.elapsed_time(b) / reps
+        del fns
     shapes = {"ln": (rows, hid), "sm": (smb, smh, sms), "gelu": (grows, gcols)}
-    return ms_step, per, bytes_model(shapes, n, mb), n, mb
+    return ms_step, in_step, sweep, bytes_model(shapes, n, mb), n, mb
 
 
 # ----------------------------------------------------------------------------
@@ -300,13 +347,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--n", type=int, default=None, help="optimizer shard size (default 3.67e9)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run 3 plain 1 GiB device-to-device copies (counter calibration)")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the per-kernel sweep of the fused kernels")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the hot path runs on a single MI355X at one GPU's shard shape, "
               "and runs on several GPUs are not supported.", file=sys.stderr)
         sys.exit(2)
 
-    ms_step, per, bts, n, mb = run_gpu(args)
+    ms_step, in_step, sweep, bts, n, mb = run_gpu(args)
+    per = dict(in_step)
+    per.update(sweep)
+    sweep = sweep or {}
     nfirst, nrest = 1, mb - 2
     step_bytes = (sum(bts[k] for k in ("layernorm_fwd", "layernorm_bwd", "alibi_softmax_fwd",
                                        "alibi_softmax_bwd", "bias_gelu_fwd", "bias_gelu_bwd", "adamw_step",
@@ -316,7 +369,11 @@ def main():
     for k, ms in per.items():
         gbs = bts[k] / (ms * 1e-3) / 1e9
         kernels[k] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-                      "algorithmic_bytes": bts[k]}
+                      "algorithmic_bytes": bts[k],
+                      "timing": "sweep of back-to-back launches on rotating cold inputs" if k in sweep
+                      else "events around each launch in the timed steps"}
+        if k in sweep:
+            kernels[k]["in_step_ms"] = round(in_step[k], 4)
     dom = "grad_accumulate"
     dom_gbs = bts[dom] / (per[dom] * 1e-3) / 1e9
     traffic = measured_traffic(dom)

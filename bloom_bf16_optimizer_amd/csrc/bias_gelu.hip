@@ -11,10 +11,10 @@
 //   y'(u) = s + 2k*u*s*(1-s)*(1 + 3c u^2).
 //
 // Mapping: a thread owns one 16-byte column vector (8 columns) for a strip of
-// RB rows, keeping the 8 bias values -- and, in the backward, 8 FP32 dbias
-// sums -- in registers.  Consecutive threads own consecutive vectors, so each
-// wave reads and writes 1 KiB contiguous per row.  The backward writes one
-// FP32 partial row per row strip; colsum.hip adds them in strip order.
+// rows, keeping the 8 bias values -- and, in the backward, 8 FP32 dbias sums
+// -- in registers.  Consecutive threads own consecutive vectors, so each wave
+// reads and writes 1 KiB contiguous per row.  The backward writes one FP32
+// partial row per row strip; colsum.hip adds them in strip order.
 #include "device_common.h"
 #include "host_common.h"
 #include "launch_plan.h"
@@ -74,52 +74,72 @@ __global__ __launch_bounds__(256) void gelu_fwd_kernel(const uint4* __restrict__
   }
 }
 
-// partial: [gridDim.y][cols] fp32 dbias partial sums.
+// Backward.  A workgroup is 64 column vectors (one per lane) by 4 row groups
+// (one per wave): wave w walks rows [r0 + w*RB, r0 + (w+1)*RB) of the block's
+// strip, so four times as many waves stream as with one row group per block
+// while the strip -- and with it the number of dbias partial rows -- stays at
+// 4*RB rows.  The four waves' FP32 column sums are added in wave order through
+// LDS and written as one partial row: partial[gridDim.y][cols].
 __global__ __launch_bounds__(256) void gelu_bwd_kernel(const uint4* __restrict__ dy,
                                                        const uint4* __restrict__ x,
                                                        const uint4* __restrict__ bias,
                                                        uint4* __restrict__ dx,
                                                        float* __restrict__ partial, int64_t rows,
-                                                       int vecs, int rows_per_block, GeluConsts g) {
-  const int v = blockIdx.x * blockDim.x + threadIdx.x;
-  if (v >= vecs) return;
-  float bv[8], acc[8];
-  unpack8(bias[v], bv);
+                                                       int vecs, int rows_per_wave, GeluConsts g) {
+  __shared__ float red[3][kWave][8];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int v = blockIdx.x * kWave + lane;
+  const bool active = v < vecs;
+  float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
-  const int64_t r1 = min(rows, r0 + rows_per_block);
-  for (int64_t r = r0; r < r1; r += kUnroll) {
-    uint4 xv[kUnroll], dv[kUnroll];
+  if (active) {
+    float bv[8];
+    unpack8(bias[v], bv);
+    const int64_t r0 = ((int64_t)blockIdx.y * 4 + wave) * rows_per_wave;
+    const int64_t r1 = min(rows, r0 + rows_per_wave);
+    for (int64_t r = r0; r < r1; r += kUnroll) {
+      uint4 xv[kUnroll], dv[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (r + u < r1) {
-        xv[u] = x[(r + u) * vecs + v];
-        dv[u] = dy[(r + u) * vecs + v];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (r + u < r1) {
-        float f[8], d[8], o[8];
-        unpack8(xv[u], f);
-        unpack8(dv[u], d);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float uu = f[e] + bv[e];
-          const float s = logistic_part(uu, g);
-          const float grad = fmaf(g.k2 * uu * s * (1.0f - s), fmaf(g.c3, uu * uu, 1.0f), s);
-          o[e] = d[e] * grad;
-          acc[e] += o[e];
+      for (int u = 0; u < kUnroll; ++u) {
+        if (r + u < r1) {
+          xv[u] = x[(r + u) * vecs + v];
+          dv[u] = dy[(r + u) * vecs + v];
         }
-        dx[(r + u) * vecs + v] = pack8(o);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (r + u < r1) {
+          float f[8], d[8], o[8];
+          unpack8(xv[u], f);
+          unpack8(dv[u], d);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float uu = f[e] + bv[e];
+            const float s = logistic_part(uu, g);
+            const float grad = fmaf(g.k2 * uu * s * (1.0f - s), fmaf(g.c3, uu * uu, 1.0f), s);
+            o[e] = d[e] * grad;
+            acc[e] += o[e];
+          }
+          dx[(r + u) * vecs + v] = pack8(o);
+        }
       }
     }
   }
-  const int64_t cols = (int64_t)vecs * 8;
-  float4* out = reinterpret_cast<float4*>(partial + (int64_t)blockIdx.y * cols + (int64_t)v * 8);
-  out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  out[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  if (wave > 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wave - 1][lane][e] = acc[e];
+  }
+  __syncthreads();
+  if (wave == 0 && active) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = ((acc[e] + red[0][lane][e]) + red[1][lane][e]) + red[2][lane][e];
+    const int64_t cols = (int64_t)vecs * 8;
+    float4* out = reinterpret_cast<float4*>(partial + (int64_t)blockIdx.y * cols + (int64_t)v * 8);
+    out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    out[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
 }
 
 GeluConsts gelu_consts() {
@@ -146,7 +166,8 @@ GeluPlan plan_gelu(int64_t rows, int vecs, int rows_per_block) {
 }
 
 constexpr int kFwdRows = 8;
-constexpr int kBwdRows = 32;
+constexpr int kBwdRowsPerWave = 8;
+constexpr int kBwdRows = 4 * kBwdRowsPerWave;  // rows per workgroup strip (one dbias partial row)
 
 bloom_status check_gelu(int64_t rows, int64_t cols) {
   BLOOM_REQUIRE(rows >= 0, BLOOM_ERR_SHAPE, "rows = %lld is negative", (long long)rows);
@@ -201,16 +222,16 @@ extern "C" bloom_status bloom_bias_gelu_bwd(const bloom_bf16* dy, const bloom_bf
   BLOOM_REQUIRE(workspace != nullptr, BLOOM_ERR_WORKSPACE, "workspace is NULL");
   BLOOM_REQUIRE(aligned16(workspace), BLOOM_ERR_ALIGN, "workspace is not 16-byte aligned");
   const int vecs = (int)(cols / 8);
-  const GeluPlan p = plan_gelu(rows, vecs, kBwdRows);
-  const size_t need = (size_t)p.grid.y * (size_t)cols * sizeof(float);
+  const dim3 grid(ceil_div(vecs, kWave), ceil_div(rows, kBwdRows));
+  const size_t need = (size_t)grid.y * (size_t)cols * sizeof(float);
   BLOOM_REQUIRE(workspace_bytes >= need, BLOOM_ERR_WORKSPACE,
                 "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   float* partial = static_cast<float*>(workspace);
-  hipLaunchKernelGGL(gelu_bwd_kernel, p.grid, p.block, 0, stream,
+  hipLaunchKernelGGL(gelu_bwd_kernel, grid, dim3(4 * kWave), 0, stream,
                      reinterpret_cast<const uint4*>(dy), reinterpret_cast<const uint4*>(x),
                      reinterpret_cast<const uint4*>(bias), reinterpret_cast<uint4*>(dx), partial,
-                     rows, vecs, p.rows_per_block, gelu_consts());
+                     rows, vecs, kBwdRowsPerWave, gelu_consts());
   if (bloom_status st = launch_status("bloom_bias_gelu_bwd")) return st;
-  launch_colsum(partial, (int)p.grid.y, cols, cols, dbias, nullptr, stream);
+  launch_colsum(partial, (int)grid.y, cols, cols, dbias, nullptr, stream);
   return launch_status("bloom_bias_gelu_bwd column sums");
 }

@@ -44,6 +44,41 @@ __device__ __forceinline__ uint4 pack8(const float f[8]) {
 }
 
 // ---------------------------------------------------------------------------
+// Streaming (non-temporal) 8- and 16-byte loads and stores.  Data that is read
+// or written once per pass and not touched again until gigabytes of other
+// traffic have gone by gains nothing from L2 or the Infinity Cache; marking
+// both its loads and its stores non-temporal raises the flat streams of the
+// optimizer from ~6.0 to ~6.6 TB/s on MI355X (marking only one side does not).
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float4 ld_nt(const float4* p) {
+  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_nt(const uint2* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void st_nt(float4* p, const float4& x) {
+  const f32x4_t v = {x.x, x.y, x.z, x.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
+}
+__device__ __forceinline__ void st_nt(uint4* p, const uint4& x) {
+  const u32x4_t v = {x.x, x.y, x.z, x.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void st_nt(uint2* p, const uint2& x) {
+  const u32x2_t v = {x.x, x.y};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
+}
+
+// ---------------------------------------------------------------------------
 // Wave64 all-reductions.  Inside each 16-lane DPP row: quad_perm [1,0,3,2],
 // quad_perm [2,3,0,1], row_half_mirror, row_mirror -- after these every lane
 // holds its row's total (each step pairs every lane with a distinct partner,

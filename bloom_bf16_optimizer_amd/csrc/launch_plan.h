@@ -23,7 +23,10 @@ struct RowPlan {
 
 inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-// Team width for a row of `vecs` vectors with at most nv_cap vectors per thread.
+// Team width for a row of `vecs` vectors with at most nv_cap vectors per
+// thread: as few idle lanes as possible, and among equally good widths the
+// widest team (fewest vectors per thread: lower register use, more waves in
+// flight per compute unit).
 inline void pick_team(int vecs, int nv_cap, int& tpr, int& nv) {
   if (vecs <= 64 * nv_cap) {
     tpr = 64;
@@ -31,7 +34,7 @@ inline void pick_team(int vecs, int nv_cap, int& tpr, int& nv) {
     return;
   }
   int best_w = 16, best_waste = 1 << 30, best_nv = 8;
-  for (int w = 2; w <= 16; ++w) {
+  for (int w = 16; w >= 2; --w) {
     const int t = 64 * w;
     const int n = ceil_div(vecs, t);
     if (n > nv_cap) continue;

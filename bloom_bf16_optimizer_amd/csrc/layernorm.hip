@@ -25,6 +25,8 @@
 namespace bloom {
 namespace {
 
+constexpr int kGammaLdsMax = 16384;  // widest row whose gamma the backward stages in LDS (32 KiB)
+
 template <int NV, int MAXB>
 __global__ __launch_bounds__(MAXB) void ln_fwd_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ gamma, const uint4* __restrict__ beta,
@@ -40,19 +42,14 @@ __global__ __launch_bounds__(MAXB) void ln_fwd_kernel(
   const int nwaves = blockDim.x / kWave;
   const uint4* xr = x + row * vecs;
 
-  uint4 xv[NV], gv[NV], bv[NV];
+  // gamma and beta are read after the statistics: they are shared by every row
+  // (served from L2), and keeping them out of registers during the reductions
+  // lets more rows be in flight per compute unit.
+  uint4 xv[NV];
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     const int v = t + k * tpr;
-    if (v < vecs) {
-      xv[k] = xr[v];
-      gv[k] = gamma[v];
-      bv[k] = beta[v];
-    } else {
-      xv[k] = make_uint4(0u, 0u, 0u, 0u);
-      gv[k] = xv[k];
-      bv[k] = xv[k];
-    }
+    xv[k] = (v < vecs) ? xr[v] : make_uint4(0u, 0u, 0u, 0u);
   }
 
   float s = 0.f;
@@ -89,8 +86,8 @@ __global__ __launch_bounds__(MAXB) void ln_fwd_kernel(
     if (v < vecs) {
       float f[8], g[8], b[8], o[8];
       unpack8(xv[k], f);
-      unpack8(gv[k], g);
-      unpack8(bv[k], b);
+      unpack8(gamma[v], g);
+      unpack8(beta[v], b);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = fmaf((f[e] - mu) * r, g[e], b[e]);
       yr[v] = pack8(o);
@@ -103,14 +100,18 @@ __global__ __launch_bounds__(MAXB) void ln_fwd_kernel(
 }
 
 // partial: [gridDim.x][2*H] fp32 -- dgamma partials then dbeta partials.
-// Dynamic LDS (wave mode with several teams only): 2*H floats.
+// Dynamic LDS: gamma as bf16 (2*H bytes, when H <= kGammaLdsMax), then, in
+// wave mode with several teams, 2*H floats for combining the teams' column sums.
 template <int NV, int MAXB>
 __global__ __launch_bounds__(MAXB) void ln_bwd_kernel(
     const uint4* __restrict__ dy, const uint4* __restrict__ x, const uint4* __restrict__ gamma,
     const float* __restrict__ mean, const float* __restrict__ rstd, uint4* __restrict__ dx,
     float* __restrict__ partial, int64_t rows, int vecs, int tpr, float hidden) {
   __shared__ float lds[2 * kMaxWaves];
-  extern __shared__ float combine[];
+  extern __shared__ uint4 dyn_lds[];
+  const bool gamma_staged = vecs * 8 <= kGammaLdsMax;
+  uint4* gamma_lds = dyn_lds;                                                  // [vecs]
+  float* combine = reinterpret_cast<float*>(dyn_lds + (gamma_staged ? vecs : 0));  // [2*H] (wave mode)
   const bool wave_rows = (tpr == kWave);
   const int teams = wave_rows ? (int)(blockDim.x / kWave) : 1;
   const int team = wave_rows ? (int)(threadIdx.x / kWave) : 0;
@@ -118,12 +119,19 @@ __global__ __launch_bounds__(MAXB) void ln_bwd_kernel(
   const int nwaves = blockDim.x / kWave;
   const int64_t team_count = (int64_t)gridDim.x * teams;
 
-  uint4 gv[NV];
+  // gamma is shared by every row: staged once in LDS, so reading it in the
+  // row loop does not wait on the vector-memory counter that also tracks the
+  // next row's prefetched loads.  (Rows wider than kGammaLdsMax read it from
+  // global memory instead.)
+  const uint4* gsrc = gamma;
+  if (gamma_staged) {
+    for (int v = threadIdx.x; v < vecs; v += blockDim.x) gamma_lds[v] = gamma[v];
+    __syncthreads();
+  }
+
   float dg[NV][8], db[NV][8];
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    const int v = t + k * tpr;
-    gv[k] = (v < vecs) ? gamma[v] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       dg[k][e] = 0.f;
@@ -162,20 +170,26 @@ __global__ __launch_bounds__(MAXB) void ln_bwd_kernel(
     }
     const float mu = mean[row];
     const float r = rstd[row];
-    // sums of g and g*x_hat (out-of-range vectors are zero and add nothing)
+    // First pass: the row sums of g and g*x_hat, and this row's share of the
+    // column sums dgamma += dy*x_hat, dbeta += dy (they need no row statistic).
     float sg = 0.f, sgx = 0.f;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-      float d[8], f[8], g[8];
-      unpack8(dv[k], d);
-      unpack8(xv[k], f);
-      unpack8(gv[k], g);
+      const int v = t + k * tpr;
+      if (v < vecs) {
+        float d[8], f[8], g[8];
+        unpack8(dv[k], d);
+        unpack8(xv[k], f);
+        unpack8(gamma_staged ? gamma_lds[v] : gsrc[v], g);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float gg = d[e] * g[e];
-        const float xh = (f[e] - mu) * r;
-        sg += gg;
-        sgx = fmaf(gg, xh, sgx);
+        for (int e = 0; e < 8; ++e) {
+          const float gg = d[e] * g[e];
+          const float xh = (f[e] - mu) * r;
+          sg += gg;
+          sgx = fmaf(gg, xh, sgx);
+          dg[k][e] = fmaf(d[e], xh, dg[k][e]);
+          db[k][e] += d[e];
+        }
       }
     }
     if (wave_rows) {
@@ -185,6 +199,7 @@ __global__ __launch_bounds__(MAXB) void ln_bwd_kernel(
     }
     const float mg = sg / hidden;
     const float mgx = sgx / hidden;
+    // Second pass: dx from the same registers.
     uint4* dxr = dx + row * vecs;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
@@ -193,13 +208,11 @@ __global__ __launch_bounds__(MAXB) void ln_bwd_kernel(
         float d[8], f[8], g[8], o[8];
         unpack8(dv[k], d);
         unpack8(xv[k], f);
-        unpack8(gv[k], g);
+        unpack8(gamma_staged ? gamma_lds[v] : gsrc[v], g);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float xh = (f[e] - mu) * r;
           o[e] = r * (d[e] * g[e] - mg - xh * mgx);
-          dg[k][e] = fmaf(d[e], xh, dg[k][e]);
-          db[k][e] += d[e];
         }
         dxr[v] = pack8(o);
       }
@@ -336,7 +349,8 @@ extern "C" bloom_status bloom_layernorm_bwd(const bloom_bf16* dy, const bloom_bf
   BLOOM_REQUIRE(workspace_bytes >= need, BLOOM_ERR_WORKSPACE,
                 "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   float* partial = static_cast<float*>(workspace);
-  const size_t lds = (p.tpr == kWave && p.block > kWave) ? 2 * (size_t)hidden * sizeof(float) : 0;
+  const size_t lds = (hidden <= kGammaLdsMax ? 2 * (size_t)hidden : 0) +
+                     ((p.tpr == kWave && p.block > kWave) ? 2 * (size_t)hidden * sizeof(float) : 0);
   const uint4* dyv = reinterpret_cast<const uint4*>(dy);
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   const uint4* gv = reinterpret_cast<const uint4*>(gamma);

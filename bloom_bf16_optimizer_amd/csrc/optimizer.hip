@@ -10,6 +10,10 @@
 // clipped at global norm 1.0); page "单机多卡实战：Megatron-DeepSpeed训练类BLOOM
 // 模型全流程解析", section 3 (the same lr, weight decay, clip and bf16 flags).
 //
+// Memory hints.  Every load and store of the streams is non-temporal: each
+// element is touched once per pass and not again until tens of gigabytes of
+// other traffic have gone by.
+//
 // Launch shape.  Every pass is a flat stream: one workgroup of 256 threads per
 // 1024 consecutive elements, each thread one "quad" of 4 elements, so every
 // wave-wide load or store instruction covers one contiguous span (512 B of
@@ -21,7 +25,7 @@
 //
 // Norm.  Every workgroup writes the FP64 sum of acc^2 over its 1024 elements
 // (exact float -> double widening, fused multiply-adds) to partials[logical
-// block]; the partials are then added in a fixed order by a 256-workgroup
+// block]; the partials are then added in a fixed order by a 2048-workgroup
 // pass and a one-workgroup finalize that forms N and the clip coefficient c,
 // which stay in device memory for the AdamW kernel (no host round trip).  The
 // partials come either from a standalone read of acc or, with no extra
@@ -37,7 +41,7 @@ namespace {
 
 constexpr int kBlock = 256;              // threads per workgroup, one quad each
 constexpr int64_t kBlockElems = 4 * kBlock;
-constexpr int kStage2Blocks = 256;       // second reduction level
+constexpr int kStage2Blocks = 2048;      // second reduction level (8 sums per finalize thread)
 
 // Workgroups of a flat pass over n elements, rounded up to a multiple of 8 so
 // that the XCD remap below is a permutation.
@@ -77,18 +81,18 @@ __global__ __launch_bounds__(kBlock) void grad_accumulate_kernel(float* __restri
   const int64_t e0 = q * 4;
   double s = 0.0;
   if (e0 + 4 <= n) {
-    const uint2 gv = reinterpret_cast<const uint2*>(g)[q];
+    const uint2 gv = ld_nt(reinterpret_cast<const uint2*>(g) + q);
     float4 r;
     if (FIRST) {
       r = make_float4(bf16_lo(gv.x), bf16_hi(gv.x), bf16_lo(gv.y), bf16_hi(gv.y));
     } else {
-      r = reinterpret_cast<const float4*>(acc)[q];
+      r = ld_nt(reinterpret_cast<const float4*>(acc) + q);
       r.x += bf16_lo(gv.x);
       r.y += bf16_hi(gv.x);
       r.z += bf16_lo(gv.y);
       r.w += bf16_hi(gv.y);
     }
-    reinterpret_cast<float4*>(acc)[q] = r;
+    st_nt(reinterpret_cast<float4*>(acc) + q, r);
     if (SUMSQ) {
       s = fma((double)r.x, (double)r.x, s);
       s = fma((double)r.y, (double)r.y, s);
@@ -117,7 +121,7 @@ __global__ __launch_bounds__(kBlock) void sumsq_kernel(const float* __restrict__
   const int64_t e0 = q * 4;
   double s = 0.0;
   if (e0 + 4 <= n) {
-    const float4 r = reinterpret_cast<const float4*>(acc)[q];
+    const float4 r = ld_nt(reinterpret_cast<const float4*>(acc) + q);
     s = fma((double)r.x, (double)r.x, s);
     s = fma((double)r.y, (double)r.y, s);
     s = fma((double)r.z, (double)r.z, s);
@@ -154,7 +158,9 @@ __global__ __launch_bounds__(kBlock) void norm_finalize_kernel(const double* __r
                                                                double max_norm,
                                                                NormState* __restrict__ state,
                                                                float* __restrict__ norm_out) {
-  const double t = block_sum_f64(part2[threadIdx.x]);
+  double s = 0.0;
+  for (int k = 0; k < kStage2Blocks / kBlock; ++k) s += part2[threadIdx.x * (kStage2Blocks / kBlock) + k];
+  const double t = block_sum_f64(s);
   if (threadIdx.x == 0) {
     const double nrm = sqrt(t);
     // NaN compares false and leaves c = 1; an infinite norm gives c = 0.
@@ -197,18 +203,18 @@ __global__ __launch_bounds__(kBlock) void adamw_kernel(float* __restrict__ maste
   const int64_t q = xcd_block() * kBlock + threadIdx.x;
   const int64_t e0 = q * 4;
   if (e0 + 4 <= n) {
-    const float4 a = reinterpret_cast<const float4*>(acc)[q];
-    float4 p = reinterpret_cast<const float4*>(master)[q];
-    float4 m = reinterpret_cast<const float4*>(exp_avg)[q];
-    float4 v = reinterpret_cast<const float4*>(exp_avg_sq)[q];
+    const float4 a = ld_nt(reinterpret_cast<const float4*>(acc) + q);
+    float4 p = ld_nt(reinterpret_cast<const float4*>(master) + q);
+    float4 m = ld_nt(reinterpret_cast<const float4*>(exp_avg) + q);
+    float4 v = ld_nt(reinterpret_cast<const float4*>(exp_avg_sq) + q);
     adam_one(a.x, c, p.x, m.x, v.x, k);
     adam_one(a.y, c, p.y, m.y, v.y, k);
     adam_one(a.z, c, p.z, m.z, v.z, k);
     adam_one(a.w, c, p.w, m.w, v.w, k);
-    reinterpret_cast<float4*>(master)[q] = p;
-    reinterpret_cast<float4*>(exp_avg)[q] = m;
-    reinterpret_cast<float4*>(exp_avg_sq)[q] = v;
-    reinterpret_cast<uint2*>(param)[q] = make_uint2(pack2(p.x, p.y), pack2(p.z, p.w));
+    st_nt(reinterpret_cast<float4*>(master) + q, p);
+    st_nt(reinterpret_cast<float4*>(exp_avg) + q, m);
+    st_nt(reinterpret_cast<float4*>(exp_avg_sq) + q, v);
+    st_nt(reinterpret_cast<uint2*>(param) + q, make_uint2(pack2(p.x, p.y), pack2(p.z, p.w)));
   } else if (e0 < n) {
     for (int64_t j = e0; j < n; ++j) {
       float p = master[j], m = exp_avg[j], v = exp_avg_sq[j];
