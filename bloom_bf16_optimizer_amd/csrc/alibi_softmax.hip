@@ -60,7 +60,7 @@ __global__ __launch_bounds__(MAXB) void softmax_fwd_kernel(
     const int v = t + k * tpr;
     if (v < nlive) {
       float s[8];
-      unpack8(src[v], s);
+      unpack8(ld_nt(src + v), s);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int j = v * 8 + e;
@@ -96,9 +96,9 @@ __global__ __launch_bounds__(MAXB) void softmax_fwd_kernel(
         float o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = z[k][e] * inv;
-        dst[v] = pack8(o);
+        st_nt(dst + v, pack8(o));
       } else {
-        dst[v] = make_uint4(0u, 0u, 0u, 0u);
+        st_nt(dst + v, make_uint4(0u, 0u, 0u, 0u));
       }
     }
   }
@@ -128,8 +128,8 @@ __global__ __launch_bounds__(MAXB) void softmax_bwd_kernel(
   for (int k = 0; k < NV; ++k) {
     const int v = t + k * tpr;
     if (v < nlive) {
-      yv[k] = ys[v];
-      dv[k] = dys[v];
+      yv[k] = ld_nt(ys + v);
+      dv[k] = ld_nt(dys + v);
     } else {
       yv[k] = make_uint4(0u, 0u, 0u, 0u);
       dv[k] = yv[k];
@@ -160,9 +160,9 @@ __global__ __launch_bounds__(MAXB) void softmax_bwd_kernel(
         unpack8(dv[k], d);
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = (v * 8 + e <= i) ? scale * y[e] * (d[e] - dot) : 0.f;
-        dst[v] = pack8(o);
+        st_nt(dst + v, pack8(o));
       } else {
-        dst[v] = make_uint4(0u, 0u, 0u, 0u);
+        st_nt(dst + v, make_uint4(0u, 0u, 0u, 0u));
       }
     }
   }

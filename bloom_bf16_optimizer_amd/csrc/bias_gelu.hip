@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void gelu_fwd_kernel(const uint4* __restrict__
     uint4 xv[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      if (r + u < r1) xv[u] = x[(r + u) * vecs + v];
+      if (r + u < r1) xv[u] = ld_nt(x + (r + u) * vecs + v);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       if (r + u < r1) {
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void gelu_fwd_kernel(const uint4* __restrict__
           const float uu = f[e] + bv[e];
           o[e] = uu * logistic_part(uu, g);
         }
-        y[(r + u) * vecs + v] = pack8(o);
+        st_nt(y + (r + u) * vecs + v, pack8(o));
       }
     }
   }
@@ -104,8 +104,8 @@ __global__ __launch_bounds__(256) void gelu_bwd_kernel(const uint4* __restrict__
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         if (r + u < r1) {
-          xv[u] = x[(r + u) * vecs + v];
-          dv[u] = dy[(r + u) * vecs + v];
+          xv[u] = ld_nt(x + (r + u) * vecs + v);
+          dv[u] = ld_nt(dy + (r + u) * vecs + v);
         }
       }
 #pragma unroll
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void gelu_bwd_kernel(const uint4* __restrict__
             o[e] = d[e] * grad;
             acc[e] += o[e];
           }
-          dx[(r + u) * vecs + v] = pack8(o);
+          st_nt(dx + (r + u) * vecs + v, pack8(o));
         }
       }
     }

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(MAXB) void ln_fwd_kernel(
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     const int v = t + k * tpr;
-    xv[k] = (v < vecs) ? xr[v] : make_uint4(0u, 0u, 0u, 0u);
+    xv[k] = (v < vecs) ? ld_nt(xr + v) : make_uint4(0u, 0u, 0u, 0u);
   }
 
   float s = 0.f;
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(MAXB) void ln_fwd_kernel(
       unpack8(beta[v], b);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = fmaf((f[e] - mu) * r, g[e], b[e]);
-      yr[v] = pack8(o);
+      st_nt(yr + v, pack8(o));
     }
   }
   if (t == 0) {
@@ -147,8 +147,8 @@ __global__ __launch_bounds__(MAXB) void ln_bwd_kernel(
   for (int k = 0; k < NV; ++k) {
     const int v = t + k * tpr;
     if (row < rows && v < vecs) {
-      dv[k] = dy[row * vecs + v];
-      xv[k] = x[row * vecs + v];
+      dv[k] = ld_nt(dy + row * vecs + v);
+      xv[k] = ld_nt(x + row * vecs + v);
     } else {
       dv[k] = make_uint4(0u, 0u, 0u, 0u);
       xv[k] = dv[k];
@@ -161,8 +161,8 @@ __global__ __launch_bounds__(MAXB) void ln_bwd_kernel(
     for (int k = 0; k < NV; ++k) {
       const int v = t + k * tpr;
       if (next < rows && v < vecs) {
-        dn[k] = dy[next * vecs + v];
-        xn[k] = x[next * vecs + v];
+        dn[k] = ld_nt(dy + next * vecs + v);
+        xn[k] = ld_nt(x + next * vecs + v);
       } else {
         dn[k] = make_uint4(0u, 0u, 0u, 0u);
         xn[k] = dn[k];
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(MAXB) void ln_bwd_kernel(
           const float xh = (f[e] - mu) * r;
           o[e] = r * (d[e] * g[e] - mg - xh * mgx);
         }
-        dxr[v] = pack8(o);
+        st_nt(dxr + v, pack8(o));
       }
     }
 #pragma unroll
