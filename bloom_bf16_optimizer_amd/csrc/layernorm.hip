@@ -263,6 +263,205 @@ __global__ __launch_bounds__(MAXB) void ln_bwd_kernel(
     *reinterpret_cast<float4*>(out + c) = *reinterpret_cast<const float4*>(combine + c);
 }
 
+// ---------------------------------------------------------------------------
+// Streaming backward for rows that one workgroup covers exactly (tpr*NV ==
+// vecs, NV <= 2, up to 16 waves): the path of the BLOOM-176B hidden sizes.
+//
+// Each wave streams its own lanes' share of the next two rows straight into
+// LDS with global_load_lds_dwordx4 (16 bytes per lane, written at
+// m0 + lane*16), so two rows are in flight while a third is computed from
+// registers.  A lane only ever reads back the 16-byte slots its own DMA wrote,
+// so the ring needs no barrier: a per-wave s_waitcnt on the vector-memory
+// counter is enough.  The DMA issue and the waits are written as inline
+// assembly with exact counts, because the compiler's own wait insertion
+// drains the whole counter at loop back-edges, which would serialise the
+// rows again.  Every vector-memory instruction a wave issues inside the row
+// loop is accounted for: per row, 2*NV DMA instructions and NV dx stores (the
+// row statistics are scalar loads, counted by lgkmcnt instead).
+//
+// Ring layout (uint4 units): [slot 2][tensor 2 (dy, x)][k NV][wave 16][lane 64].
+// The arithmetic, its order and the partial-row layout are exactly those of
+// ln_bwd_kernel for the same team, so both produce identical bits.
+typedef uint32_t u32x4_lds_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint4 lds_uint4;
+
+__device__ __forceinline__ uint32_t lds_offset(const lds_uint4* p) { return (uint32_t)(uintptr_t)p; }
+
+// One 16-byte-per-lane transfer from global memory into LDS at m0 + lane*16.
+__device__ __forceinline__ void dma16(const uint4* src, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int NV>
+__device__ __forceinline__ int ring_index(int slot, int q, int k, int w) {
+  return (((slot * 2 + q) * NV + k) * kMaxWaves + w) * kWave;
+}
+
+// Requests row `row` (or, when !live, a harmless re-read of gamma) into `slot`.
+template <int NV>
+__device__ __forceinline__ void ring_issue(lds_uint4* ring, int slot, const uint4* __restrict__ dy,
+                                           const uint4* __restrict__ x, const uint4* __restrict__ gamma,
+                                           int64_t row, bool live, int vecs, int t, int tpr, int w) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int v = t + k * tpr;
+      const uint4* src = live ? (q == 0 ? dy : x) + row * vecs + v : gamma + v;
+      dma16(src, __builtin_amdgcn_readfirstlane(lds_offset(ring + ring_index<NV>(slot, q, k, w))));
+    }
+  }
+}
+
+template <int NV>
+__device__ __forceinline__ void ring_read(const lds_uint4* ring, int slot, int w, int lane, uint4 (&d)[NV],
+                                          uint4 (&xv)[NV]) {
+  u32x4_lds_t r[2 * NV];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const uint32_t a = lds_offset(ring + ring_index<NV>(slot, q, k, w) + lane);
+      asm volatile("ds_read_b128 %0, %1" : "=v"(r[q * NV + k]) : "v"(a) : "memory");
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    d[k] = make_uint4(r[k].x, r[k].y, r[k].z, r[k].w);
+    xv[k] = make_uint4(r[NV + k].x, r[NV + k].y, r[NV + k].z, r[NV + k].w);
+  }
+}
+
+template <int NV>
+__global__ __launch_bounds__(kMaxBlock) void ln_bwd_stream_kernel(
+    const uint4* __restrict__ dy, const uint4* __restrict__ x, const uint4* __restrict__ gamma,
+    const float* __restrict__ mean, const float* __restrict__ rstd, uint4* __restrict__ dx,
+    float* __restrict__ partial, int64_t rows, int vecs, float hidden) {
+  __shared__ uint4 ring_storage[2 * 2 * NV * kMaxWaves * kWave];
+  __shared__ float red[2][2 * kMaxWaves];
+  lds_uint4* ring = (lds_uint4*)ring_storage;
+  const int t = threadIdx.x, tpr = blockDim.x, nwaves = tpr / kWave;
+  const int w = t / kWave, lane = t & (kWave - 1);
+  const int64_t first = blockIdx.x, stride = gridDim.x;
+  const int count = (int)((rows - first + stride - 1) / stride);  // >= 1: grid <= rows
+
+  // gamma lives in registers; the empty asm makes its loads complete here,
+  // before any transfer is issued, so no later wait has to cover them.
+  uint4 g[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) g[k] = gamma[t + k * tpr];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) asm volatile("" : "+v"(g[k].x), "+v"(g[k].y), "+v"(g[k].z), "+v"(g[k].w));
+  float dg[NV][8], db[NV][8];
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dg[k][e] = db[k][e] = 0.f;
+
+  ring_issue<NV>(ring, 0, dy, x, gamma, first, true, vecs, t, tpr, w);
+  ring_issue<NV>(ring, 1, dy, x, gamma, first + stride, 1 < count, vecs, t, tpr, w);
+  for (int i = 0; i < count; ++i) {
+    const int slot = i & 1;
+    // Row i's transfers are done once no more than the operations issued after
+    // them are outstanding: row 0 -> the transfers of row 1; row 1 -> those of
+    // row 2 and row 0's stores; later -> stores(i-2), transfers(i+1), stores(i-1).
+    if (i >= 2)
+      wait_vmem<4 * NV>();
+    else if (i == 1)
+      wait_vmem<3 * NV>();
+    else
+      wait_vmem<2 * NV>();
+    uint4 dv[NV], xv[NV];
+    ring_read<NV>(ring, slot, w, lane, dv, xv);
+    // The slot is free again: request row i+2 into it (a dummy past the end,
+    // so that every iteration issues the same number of operations).
+    ring_issue<NV>(ring, slot, dy, x, gamma, first + (int64_t)(i + 2) * stride, i + 2 < count, vecs, t,
+                   tpr, w);
+    const int64_t row = first + (int64_t)i * stride;
+    const float mu = mean[row];
+    const float r = rstd[row];
+    float sg = 0.f, sgx = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      float d[8], f[8], gg[8];
+      unpack8(dv[k], d);
+      unpack8(xv[k], f);
+      unpack8(g[k], gg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = d[e] * gg[e];
+        const float xh = (f[e] - mu) * r;
+        sg += p;
+        sgx = fmaf(p, xh, sgx);
+        dg[k][e] = fmaf(d[e], xh, dg[k][e]);
+        db[k][e] += d[e];
+      }
+    }
+    // Workgroup sums with one barrier: the two halves of `red` alternate, and
+    // a wave can only write a half again after every wave has passed the next
+    // barrier, i.e. after all of them have read it.
+    sg = wave_sum(sg);
+    sgx = wave_sum(sgx);
+    float* rr = red[slot];
+    if (lane == 0) {
+      rr[w] = sg;
+      rr[kMaxWaves + w] = sgx;
+    }
+    __syncthreads();
+    float a = 0.f, b = 0.f;
+    for (int k = 0; k < nwaves; ++k) {
+      a += rr[k];
+      b += rr[kMaxWaves + k];
+    }
+    const float mg = a / hidden;
+    const float mgx = b / hidden;
+    uint4* dxr = dx + row * vecs;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      float d[8], f[8], gg[8], o[8];
+      unpack8(dv[k], d);
+      unpack8(xv[k], f);
+      unpack8(g[k], gg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xh = (f[e] - mu) * r;
+        o[e] = r * (d[e] * gg[e] - mg - xh * mgx);
+      }
+      st_nt(dxr + t + k * tpr, pack8(o));
+    }
+    asm volatile("" ::: "memory");  // keeps the stores inside this iteration's count
+  }
+  // The trailing dummy transfers must land before the workgroup's LDS is released.
+  wait_vmem<0>();
+
+  const int hidden_i = vecs * 8;
+  float* out = partial + (int64_t)blockIdx.x * 2 * hidden_i;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int v = t + k * tpr;
+    float4* og = reinterpret_cast<float4*>(out + v * 8);
+    float4* ob = reinterpret_cast<float4*>(out + hidden_i + v * 8);
+    og[0] = make_float4(dg[k][0], dg[k][1], dg[k][2], dg[k][3]);
+    og[1] = make_float4(dg[k][4], dg[k][5], dg[k][6], dg[k][7]);
+    ob[0] = make_float4(db[k][0], db[k][1], db[k][2], db[k][3]);
+    ob[1] = make_float4(db[k][4], db[k][5], db[k][6], db[k][7]);
+  }
+}
+
+// The streaming backward applies when a block-mode team covers the row with
+// no idle lane and two vectors per thread at most.
+inline bool use_stream_bwd(const RowPlan& p, int vecs) {
+  return p.tpr > kWave && p.block == p.tpr && p.tpr <= kMaxBlock && p.nv <= 2 && p.tpr * p.nv == vecs;
+}
+
 template <int NV, int MAXB>
 void launch_fwd(const RowPlan& p, hipStream_t s, const uint4* x, const uint4* g, const uint4* b,
                 uint4* y, float* mean, float* rstd, int64_t rows, int vecs, float eps) {
@@ -355,10 +554,19 @@ extern "C" bloom_status bloom_layernorm_bwd(const bloom_bf16* dy, const bloom_bf
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   const uint4* gv = reinterpret_cast<const uint4*>(gamma);
   uint4* dxv = reinterpret_cast<uint4*>(dx);
+  if (use_stream_bwd(p, vecs)) {
+    if (p.nv == 1)
+      hipLaunchKernelGGL((ln_bwd_stream_kernel<1>), dim3(p.grid), dim3(p.block), 0, stream, dyv, xv, gv, mean,
+                         rstd, dxv, partial, rows, vecs, (float)hidden);
+    else
+      hipLaunchKernelGGL((ln_bwd_stream_kernel<2>), dim3(p.grid), dim3(p.block), 0, stream, dyv, xv, gv, mean,
+                         rstd, dxv, partial, rows, vecs, (float)hidden);
+  } else {
 #define CALL(NV, MAXB) \
   launch_bwd<NV, MAXB>(p, stream, dyv, xv, gv, mean, rstd, dxv, partial, rows, vecs, lds)
-  BLOOM_ROW_DISPATCH(p, CALL);
+    BLOOM_ROW_DISPATCH(p, CALL);
 #undef CALL
+  }
   if (bloom_status st = launch_status("bloom_layernorm_bwd")) return st;
   launch_colsum(partial, p.grid, 2 * hidden, hidden, dgamma, dbeta, stream);
   return launch_status("bloom_layernorm_bwd column sums");
