@@ -14,6 +14,7 @@ namespace {
 
 constexpr int kQuads = 16;
 constexpr int kLanes = 16;
+constexpr int kBatch = 8;
 
 __global__ __launch_bounds__(kQuads* kLanes) void colsum_kernel(const float* __restrict__ partial,
                                                                 int parts, int64_t cols,
@@ -26,12 +27,25 @@ __global__ __launch_bounds__(kQuads* kLanes) void colsum_kernel(const float* __r
   const int64_t c = ((int64_t)blockIdx.x * kQuads + q) * 4;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   if (c < cols) {
-    for (int p = lane; p < parts; p += kLanes) {
-      const float4 v = *reinterpret_cast<const float4*>(partial + (int64_t)p * cols + c);
-      s.x += v.x;
-      s.y += v.y;
-      s.z += v.z;
-      s.w += v.w;
+    // kBatch loads are issued before any of them is added, so a lane keeps
+    // that many requests in flight; the additions still run in row order.
+    for (int p0 = lane; p0 < parts; p0 += kLanes * kBatch) {
+      float4 v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int p = p0 + u * kLanes;
+        v[u] = (p < parts) ? *reinterpret_cast<const float4*>(partial + (int64_t)p * cols + c)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (p0 + u * kLanes < parts) {
+          s.x += v[u].x;
+          s.y += v[u].y;
+          s.z += v[u].z;
+          s.w += v[u].w;
+        }
+      }
     }
   }
   acc[lane][q] = s;

@@ -49,9 +49,37 @@ inline void pick_team(int vecs, int nv_cap, int& tpr, int& nv) {
   nv = best_nv;
 }
 
+// Forward team: as few idle lanes as possible, and among equally good widths
+// the NARROWEST (most vectors per thread).  The forward holds only its own row
+// in registers, so the bytes a compute unit keeps in flight grow with the
+// vectors per thread faster than the register cost cuts the resident waves
+// (e.g. H = 14336: 256 threads x 7 vectors keeps ~140 KB per CU in flight,
+// 896 x 2 only ~64 KB).
+inline void pick_team_narrow(int vecs, int nv_cap, int& tpr, int& nv) {
+  if (vecs <= 64 * nv_cap) {
+    tpr = 64;
+    nv = ceil_div(vecs, 64);
+    return;
+  }
+  int best_w = 16, best_waste = 1 << 30, best_nv = nv_cap;
+  for (int w = 2; w <= 16; ++w) {
+    const int t = 64 * w;
+    const int n = ceil_div(vecs, t);
+    if (n > nv_cap) continue;
+    const int waste = t * n - vecs;
+    if (waste < best_waste) {
+      best_waste = waste;
+      best_w = w;
+      best_nv = n;
+    }
+  }
+  tpr = 64 * best_w;
+  nv = best_nv;
+}
+
 inline RowPlan plan_rows_fwd(int64_t rows, int vecs) {
   RowPlan p;
-  pick_team(vecs, 8, p.tpr, p.nv);
+  pick_team_narrow(vecs, 8, p.tpr, p.nv);
   if (p.tpr == 64) {
     p.block = 256;
     p.grid = ceil_div(rows, p.block / 64);
