@@ -8,13 +8,20 @@
 //   (1 + tanh(a))/2 = 1/(1 + exp(-2a)),
 // so y = u*s with s = 1/(1 + exp2(u*(A + B u^2))), A = -2k*log2(e),
 // B = -2kc*log2(e); and the derivative becomes
-//   y'(u) = s + 2k*u*s*(1-s)*(1 + 3c u^2).
+//   y'(u) = s + [u*(2k + 6kc u^2)] * [s(1-s)],
+// evaluated as fma(p, q, s) with q = fma(-s, s, s) and p = u*fma(6kc, u^2, 2k)
+// (u^2 is shared with the exponent).
 //
 // Mapping: a thread owns one 16-byte column vector (8 columns) for a strip of
 // rows, keeping the 8 bias values -- and, in the backward, 8 FP32 dbias sums
 // -- in registers.  Consecutive threads own consecutive vectors, so each wave
 // reads and writes 1 KiB contiguous per row.  The backward writes one FP32
 // partial row per row strip; colsum.hip adds them in strip order.
+//
+// Latency: a full strip issues all of its row loads before the first row is
+// computed (straight-line code, no guards), so the compiler can wait for each
+// row with a partial vmcnt; the backward runs its strip as a two-deep stage
+// pipeline, the loads of stage k+2 in flight while stage k is computed.
 #include "device_common.h"
 #include "host_common.h"
 #include "launch_plan.h"
@@ -25,52 +32,83 @@ namespace {
 constexpr double kKd = 0.7978845608028654;
 constexpr double kCd = 0.044715;
 constexpr double kLog2e = 1.4426950408889634;
-constexpr int kUnroll = 4;
+constexpr int kFwdRows = 4;                              // rows per forward strip
+constexpr int kBwdStageRows = 2;                         // rows per backward stage
+constexpr int kBwdStages = 4;                            // stages per wave
+constexpr int kBwdRowsPerWave = kBwdStageRows * kBwdStages;
+constexpr int kBwdRows = 4 * kBwdRowsPerWave;            // rows per workgroup strip (one dbias partial row)
 
 struct GeluConsts {
   float a;     // -2k log2(e)
   float b;     // -2kc log2(e)
   float k2;    // 2k
-  float c3;    // 3c
+  float k6c;   // 6kc
 };
 
 // s = 1/(1 + exp(-2a)) with the hardware exp2 and reciprocal (each within
 // 1 ulp of fp32; exp2 results below 2^-126 flush to 0, which leaves s = 1).
 // The element budget is tight: at 8 TB/s the forward has ~20 VALU slots per
 // element, so the correctly rounded divide (about 10 instructions) is not used.
-__device__ __forceinline__ float logistic_part(float u, const GeluConsts& g) {
-  const float t = __builtin_amdgcn_exp2f(u * fmaf(g.b, u * u, g.a));
+__device__ __forceinline__ float logistic_part(float u, float u2, const GeluConsts& g) {
+  const float t = __builtin_amdgcn_exp2f(u * fmaf(g.b, u2, g.a));
   return __builtin_amdgcn_rcpf(1.0f + t);
 }
 
+__device__ __forceinline__ float gelu_value(float u, const GeluConsts& g) {
+  return u * logistic_part(u, u * u, g);
+}
+
+__device__ __forceinline__ float gelu_slope(float u, const GeluConsts& g) {
+  const float u2 = u * u;
+  const float s = logistic_part(u, u2, g);
+  const float q = fmaf(-s, s, s);             // s(1-s)
+  const float p = u * fmaf(g.k6c, u2, g.k2);  // 2k u (1 + 3c u^2)
+  return fmaf(p, q, s);
+}
+
+__device__ __forceinline__ uint4 gelu_row(const uint4& xv, const float (&bv)[8], const GeluConsts& g) {
+  float f[8], o[8];
+  unpack8(xv, f);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = gelu_value(f[e] + bv[e], g);
+  return pack8(o);
+}
+
+__device__ __forceinline__ uint4 gelu_grad_row(const uint4& dv, const uint4& xv, const float (&bv)[8],
+                                               float (&acc)[8], const GeluConsts& g) {
+  float f[8], d[8], o[8];
+  unpack8(xv, f);
+  unpack8(dv, d);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    o[e] = d[e] * gelu_slope(f[e] + bv[e], g);
+    acc[e] += o[e];
+  }
+  return pack8(o);
+}
+
+// Forward: a 1-D grid of (row strip, column block) pairs, column block
+// fastest, so consecutive workgroups sweep whole rows of kFwdRows rows
+// (contiguous memory) and the grid has no 65535 limit on the row strips.
 __global__ __launch_bounds__(256) void gelu_fwd_kernel(const uint4* __restrict__ x,
                                                        const uint4* __restrict__ bias,
-                                                       uint4* __restrict__ y, int64_t rows,
-                                                       int vecs, int rows_per_block, GeluConsts g) {
-  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+                                                       uint4* __restrict__ y, int64_t rows, int vecs,
+                                                       int col_blocks, GeluConsts g) {
+  const int cb = (int)(blockIdx.x % (unsigned)col_blocks);
+  const int64_t strip = blockIdx.x / (unsigned)col_blocks;
+  const int v = cb * blockDim.x + threadIdx.x;
   if (v >= vecs) return;
   float bv[8];
   unpack8(bias[v], bv);
-  const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
-  const int64_t r1 = min(rows, r0 + rows_per_block);
-  for (int64_t r = r0; r < r1; r += kUnroll) {
-    uint4 xv[kUnroll];
+  const int64_t r0 = strip * kFwdRows;
+  if (r0 + kFwdRows <= rows) {
+    uint4 xv[kFwdRows];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (r + u < r1) xv[u] = ld_nt(x + (r + u) * vecs + v);
+    for (int u = 0; u < kFwdRows; ++u) xv[u] = ld_nt(x + (r0 + u) * vecs + v);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (r + u < r1) {
-        float f[8], o[8];
-        unpack8(xv[u], f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float uu = f[e] + bv[e];
-          o[e] = uu * logistic_part(uu, g);
-        }
-        st_nt(y + (r + u) * vecs + v, pack8(o));
-      }
-    }
+    for (int u = 0; u < kFwdRows; ++u) st_nt(y + (r0 + u) * vecs + v, gelu_row(xv[u], bv, g));
+  } else {
+    for (int64_t r = r0; r < rows; ++r) st_nt(y + r * vecs + v, gelu_row(ld_nt(x + r * vecs + v), bv, g));
   }
 }
 
@@ -85,7 +123,7 @@ __global__ __launch_bounds__(256) void gelu_bwd_kernel(const uint4* __restrict__
                                                        const uint4* __restrict__ bias,
                                                        uint4* __restrict__ dx,
                                                        float* __restrict__ partial, int64_t rows,
-                                                       int vecs, int rows_per_wave, GeluConsts g) {
+                                                       int vecs, GeluConsts g) {
   __shared__ float red[3][kWave][8];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -97,34 +135,38 @@ __global__ __launch_bounds__(256) void gelu_bwd_kernel(const uint4* __restrict__
   if (active) {
     float bv[8];
     unpack8(bias[v], bv);
-    const int64_t r0 = ((int64_t)blockIdx.y * 4 + wave) * rows_per_wave;
-    const int64_t r1 = min(rows, r0 + rows_per_wave);
-    for (int64_t r = r0; r < r1; r += kUnroll) {
-      uint4 xv[kUnroll], dv[kUnroll];
+    const int64_t r0 = ((int64_t)blockIdx.y * 4 + wave) * kBwdRowsPerWave;
+    if (r0 + kBwdRowsPerWave <= rows) {
+      // kBwdStages stages of kBwdStageRows rows; two stages of loads in flight.
+      uint4 xv[2][kBwdStageRows], dv[2][kBwdStageRows];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (r + u < r1) {
-          xv[u] = ld_nt(x + (r + u) * vecs + v);
-          dv[u] = ld_nt(dy + (r + u) * vecs + v);
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int u = 0; u < kBwdStageRows; ++u) {
+          const int64_t r = r0 + st * kBwdStageRows + u;
+          xv[st][u] = ld_nt(x + r * vecs + v);
+          dv[st][u] = ld_nt(dy + r * vecs + v);
         }
-      }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (r + u < r1) {
-          float f[8], d[8], o[8];
-          unpack8(xv[u], f);
-          unpack8(dv[u], d);
+      for (int st = 0; st < kBwdStages; ++st) {
+        const int b = st & 1;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float uu = f[e] + bv[e];
-            const float s = logistic_part(uu, g);
-            const float grad = fmaf(g.k2 * uu * s * (1.0f - s), fmaf(g.c3, uu * uu, 1.0f), s);
-            o[e] = d[e] * grad;
-            acc[e] += o[e];
+        for (int u = 0; u < kBwdStageRows; ++u) {
+          const int64_t r = r0 + st * kBwdStageRows + u;
+          st_nt(dx + r * vecs + v, gelu_grad_row(dv[b][u], xv[b][u], bv, acc, g));
+        }
+        if (st + 2 < kBwdStages) {
+#pragma unroll
+          for (int u = 0; u < kBwdStageRows; ++u) {
+            const int64_t r = r0 + (st + 2) * kBwdStageRows + u;
+            xv[b][u] = ld_nt(x + r * vecs + v);
+            dv[b][u] = ld_nt(dy + r * vecs + v);
           }
-          st_nt(dx + (r + u) * vecs + v, pack8(o));
         }
       }
+    } else {
+      for (int64_t r = r0; r < rows && r < r0 + kBwdRowsPerWave; ++r)
+        st_nt(dx + r * vecs + v, gelu_grad_row(ld_nt(dy + r * vecs + v), ld_nt(x + r * vecs + v), bv, acc, g));
     }
   }
   if (wave > 0) {
@@ -147,34 +189,16 @@ GeluConsts gelu_consts() {
   g.a = (float)(-2.0 * kKd * kLog2e);
   g.b = (float)(-2.0 * kKd * kCd * kLog2e);
   g.k2 = (float)(2.0 * kKd);
-  g.c3 = (float)(3.0 * kCd);
+  g.k6c = (float)(6.0 * kKd * kCd);
   return g;
 }
-
-struct GeluPlan {
-  dim3 grid, block;
-  int rows_per_block;
-};
-
-GeluPlan plan_gelu(int64_t rows, int vecs, int rows_per_block) {
-  GeluPlan p;
-  const int threads = vecs < 256 ? ((vecs + 63) / 64) * 64 : 256;
-  p.block = dim3(threads);
-  p.rows_per_block = rows_per_block;
-  p.grid = dim3(ceil_div(vecs, threads), ceil_div(rows, rows_per_block));
-  return p;
-}
-
-constexpr int kFwdRows = 8;
-constexpr int kBwdRowsPerWave = 8;
-constexpr int kBwdRows = 4 * kBwdRowsPerWave;  // rows per workgroup strip (one dbias partial row)
 
 bloom_status check_gelu(int64_t rows, int64_t cols) {
   BLOOM_REQUIRE(rows >= 0, BLOOM_ERR_SHAPE, "rows = %lld is negative", (long long)rows);
   BLOOM_REQUIRE(cols >= 8 && cols <= BLOOM_MAX_HIDDEN && cols % 8 == 0, BLOOM_ERR_SHAPE,
                 "cols = %lld must be a multiple of 8 in [8, %d]", (long long)cols,
                 BLOOM_MAX_HIDDEN);
-  BLOOM_REQUIRE(rows <= (int64_t)kFwdRows * 65535, BLOOM_ERR_SHAPE, "rows = %lld too large",
+  BLOOM_REQUIRE(rows <= (int64_t)kBwdRows * 65535, BLOOM_ERR_SHAPE, "rows = %lld too large",
                 (long long)rows);
   return BLOOM_OK;
 }
@@ -194,10 +218,13 @@ extern "C" bloom_status bloom_bias_gelu_fwd(const bloom_bf16* x, const bloom_bf1
   BLOOM_REQUIRE_PTR(bias);
   BLOOM_REQUIRE_PTR(y);
   const int vecs = (int)(cols / 8);
-  const GeluPlan p = plan_gelu(rows, vecs, kFwdRows);
-  hipLaunchKernelGGL(gelu_fwd_kernel, p.grid, p.block, 0, stream,
+  const int threads = vecs < 256 ? ((vecs + 63) / 64) * 64 : 256;
+  const int col_blocks = ceil_div(vecs, threads);
+  const int64_t blocks = (int64_t)ceil_div(rows, kFwdRows) * col_blocks;
+  BLOOM_REQUIRE(blocks <= 0x7fffffff, BLOOM_ERR_SHAPE, "rows = %lld too large", (long long)rows);
+  hipLaunchKernelGGL(gelu_fwd_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
                      reinterpret_cast<const uint4*>(x), reinterpret_cast<const uint4*>(bias),
-                     reinterpret_cast<uint4*>(y), rows, vecs, p.rows_per_block, gelu_consts());
+                     reinterpret_cast<uint4*>(y), rows, vecs, col_blocks, gelu_consts());
   return launch_status("bloom_bias_gelu_fwd");
 }
 
@@ -230,7 +257,7 @@ extern "C" bloom_status bloom_bias_gelu_bwd(const bloom_bf16* dy, const bloom_bf
   hipLaunchKernelGGL(gelu_bwd_kernel, grid, dim3(4 * kWave), 0, stream,
                      reinterpret_cast<const uint4*>(dy), reinterpret_cast<const uint4*>(x),
                      reinterpret_cast<const uint4*>(bias), reinterpret_cast<uint4*>(dx), partial,
-                     rows, vecs, kBwdRowsPerWave, gelu_consts());
+                     rows, vecs, gelu_consts());
   if (bloom_status st = launch_status("bloom_bias_gelu_bwd")) return st;
   launch_colsum(partial, (int)grid.y, cols, cols, dbias, nullptr, stream);
   return launch_status("bloom_bias_gelu_bwd column sums");
