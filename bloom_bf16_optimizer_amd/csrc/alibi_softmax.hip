@@ -53,23 +53,31 @@ __global__ __launch_bounds__(MAXB) void softmax_fwd_kernel(
   uint4* dst = probs + row * vecs;
   const int nlive = (i >> 3) + 1;  // vectors holding some column j <= i
 
+  // Loads without per-lane branches: a vector past the causal window
+  // (v >= nlive, so every column j = 8v+e > i) re-reads the row's first
+  // vector -- the same cache line for all such lanes, no extra HBM bytes --
+  // and is masked by j <= i; only a k whose vectors are all past the window
+  // for the whole team is skipped (a team-uniform branch).  The NV loads are
+  // all in flight before the first is used.
+  uint4 raw[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int v = t + k * tpr;
+    raw[k] = make_uint4(0u, 0u, 0u, 0u);
+    if (k * tpr < nlive) raw[k] = ld_nt(src + (v < nlive ? v : 0));  // team-uniform test
+  }
   float z[NV][8];
   float mx = -INFINITY;
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     const int v = t + k * tpr;
-    if (v < nlive) {
-      float s[8];
-      unpack8(ld_nt(src + v), s);
+    float s[8];
+    unpack8(raw[k], s);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = v * 8 + e;
-        z[k][e] = (j <= i) ? fmaf(s[e], scale2, slope2 * (float)(j - i)) : -INFINITY;
-        mx = fmaxf(mx, z[k][e]);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) z[k][e] = -INFINITY;
+    for (int e = 0; e < 8; ++e) {
+      const int j = v * 8 + e;
+      z[k][e] = (j <= i) ? fmaf(s[e], scale2, slope2 * (float)(j - i)) : -INFINITY;
+      mx = fmaxf(mx, z[k][e]);
     }
   }
   mx = wave_rows ? wave_max(mx) : block_max(mx, lds, nwaves);
@@ -92,14 +100,10 @@ __global__ __launch_bounds__(MAXB) void softmax_fwd_kernel(
   for (int k = 0; k < NV; ++k) {
     const int v = t + k * tpr;
     if (v < vecs) {
-      if (v < nlive) {
-        float o[8];
+      float o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = z[k][e] * inv;
-        st_nt(dst + v, pack8(o));
-      } else {
-        st_nt(dst + v, make_uint4(0u, 0u, 0u, 0u));
-      }
+      for (int e = 0; e < 8; ++e) o[e] = z[k][e] * inv;  // masked: exp2(-inf) * inv = +0
+      st_nt(dst + v, pack8(o));
     }
   }
 }
@@ -123,30 +127,30 @@ __global__ __launch_bounds__(MAXB) void softmax_bwd_kernel(
   uint4* dst = dscores + row * vecs;
   const int nlive = (i >> 3) + 1;
 
+  // Loads as in the forward: lanes past the causal window re-read vector 0
+  // and are masked by j <= i.
   uint4 yv[NV], dv[NV];
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     const int v = t + k * tpr;
-    if (v < nlive) {
-      yv[k] = ld_nt(ys + v);
-      dv[k] = ld_nt(dys + v);
-    } else {
-      yv[k] = make_uint4(0u, 0u, 0u, 0u);
-      dv[k] = yv[k];
+    const int vv = v < nlive ? v : 0;
+    yv[k] = make_uint4(0u, 0u, 0u, 0u);
+    dv[k] = yv[k];
+    if (k * tpr < nlive) {  // team-uniform test
+      yv[k] = ld_nt(ys + vv);
+      dv[k] = ld_nt(dys + vv);
     }
   }
   float dot = 0.f;
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     const int v = t + k * tpr;
-    if (v < nlive) {
-      float y[8], d[8];
-      unpack8(yv[k], y);
-      unpack8(dv[k], d);
+    float y[8], d[8];
+    unpack8(yv[k], y);
+    unpack8(dv[k], d);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (v * 8 + e <= i) dot = fmaf(y[e], d[e], dot);
-    }
+    for (int e = 0; e < 8; ++e)
+      if (v * 8 + e <= i) dot = fmaf(y[e], d[e], dot);
   }
   dot = wave_rows ? wave_sum(dot) : block_sum(dot, lds, nwaves);
 
@@ -154,16 +158,12 @@ __global__ __launch_bounds__(MAXB) void softmax_bwd_kernel(
   for (int k = 0; k < NV; ++k) {
     const int v = t + k * tpr;
     if (v < vecs) {
-      if (v < nlive) {
-        float y[8], d[8], o[8];
-        unpack8(yv[k], y);
-        unpack8(dv[k], d);
+      float y[8], d[8], o[8];
+      unpack8(yv[k], y);
+      unpack8(dv[k], d);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (v * 8 + e <= i) ? scale * y[e] * (d[e] - dot) : 0.f;
-        st_nt(dst + v, pack8(o));
-      } else {
-        st_nt(dst + v, make_uint4(0u, 0u, 0u, 0u));
-      }
+      for (int e = 0; e < 8; ++e) o[e] = (v * 8 + e <= i) ? scale * y[e] * (d[e] - dot) : 0.f;
+      st_nt(dst + v, pack8(o));
     }
   }
 }
