@@ -16,6 +16,16 @@ g = dy*gamma,
 The ``*_f64`` functions take and return float64 arrays.  The others take bf16
 bit patterns, compute in float64 and round each bf16 output once at the end;
 mean and rstd are returned as float32.
+
+Residual form: section 4.3 of page "企业官网建设流程全解析" fuses LayerNorm
+with the residual connection (its kernel is a stub taking output, input,
+residual, gamma, beta).  Reading used (BLOOM's blocks are pre-LN, so the sum
+is also the residual stream the next block adds to): h = bf16(x + r) is
+written out, and y = LayerNorm(h) -- the LayerNorm of the rounded sum, so the
+fused operation equals "residual add, then LayerNorm" exactly.  Its backward
+takes dy and dres (the gradient reaching h through the residual stream) and
+returns dh = dLN(dy; h) + dres, rounded once, which is the gradient of both x
+and r; dgamma and dbeta are those of the LayerNorm of h.
 """
 
 from __future__ import annotations
@@ -106,3 +116,47 @@ def layernorm_bwd(dy_bits, x_bits, gamma_bits, eps: float, return_f64: bool = Fa
     x_hat = (x - mu[:, None]) * r[:, None]
     col_terms = (np.abs(dy * x_hat).sum(axis=0), np.abs(dy).sum(axis=0))
     return out, (dx, dgamma, dbeta, terms, col_terms)
+
+
+def residual_add(x_bits, r_bits):
+    """h = x + r rounded once to bf16 (the sum of two bf16 values is exact in float64)."""
+    return round_to_bf16(to_f64(x_bits) + to_f64(r_bits))
+
+
+def layernorm_residual_fwd(x_bits, r_bits, gamma_bits, beta_bits, eps: float, return_f64: bool = False):
+    """(h, y, mean, rstd): h = bf16(x + r) and the LayerNorm of h.
+
+    With ``return_f64`` returns ((h, y, mean, rstd), (y_f64, y_terms)) as
+    layernorm_fwd does for the normalised part.
+    """
+    h = residual_add(x_bits, r_bits)
+    res = layernorm_fwd(h, gamma_bits, beta_bits, eps, return_f64=return_f64)
+    if not return_f64:
+        return (h,) + tuple(res)
+    (y, mu, r), f64 = res
+    return (h, y, mu, r), f64
+
+
+def layernorm_residual_bwd_f64(dy, dres, h, gamma, eps: float):
+    """dh = dLN(dy; h) + dres, dgamma, dbeta and dh's condition magnitude (float64)."""
+    dx, dgamma, dbeta, terms = layernorm_bwd_f64(dy, h, gamma, eps)
+    return dx + dres, dgamma, dbeta, terms + np.abs(dres)
+
+
+def layernorm_residual_bwd(dy_bits, dres_bits, h_bits, gamma_bits, eps: float, return_f64: bool = False):
+    """dh, dgamma, dbeta as bf16 bits (statistics recomputed in float64 from h).
+
+    With ``return_f64`` also returns (dh, dgamma, dbeta, dh_terms,
+    (sum|dy x_hat|, sum|dy|)) in float64.
+    """
+    h = to_f64(h_bits)
+    dy = to_f64(dy_bits)
+    eps64 = _eps64(eps)
+    dh, dgamma, dbeta, terms = layernorm_residual_bwd_f64(dy, to_f64(dres_bits), h, to_f64(gamma_bits), eps64)
+    out = (round_to_bf16(dh), round_to_bf16(dgamma), round_to_bf16(dbeta))
+    if not return_f64:
+        return out
+    mu, r = stats_f64(h, eps64)
+    x_hat = (h - mu[:, None]) * r[:, None]
+    col_terms = (np.abs(dy * x_hat).sum(axis=0), np.abs(dy).sum(axis=0))
+    return out, (dh, dgamma, dbeta, terms, col_terms)

@@ -119,3 +119,61 @@ def test_backward_matches_torch_autograd():
     assert np.allclose(db, tb.grad.numpy(), rtol=1e-10, atol=1e-12)
     assert np.array_equal(dxb, round_to_bf16(tx.grad.numpy())) or \
         np.all(np.abs(to_f64(dxb) - tx.grad.numpy()) <= 0.5 * ulp(dxb) + 1e-12)
+
+
+# Residual form (section 4.3 of page "企业官网建设流程全解析": LayerNorm fused
+# with the residual connection; h = bf16(x + r), y = LayerNorm(h)).
+
+def test_residual_add_rounds_once_to_nearest_even():
+    # 1 + 2^-8 lies halfway between bf16 1.0 (0x3F80) and 1.0078125 (0x3F81):
+    # ties go to the even pattern; a hair above the tie rounds up.
+    x = np.array([0x3F80, 0x3F81, 0x3F80, 0x3F80, 0xBF81], dtype=np.uint16)
+    r = np.array([0x3B80, 0x3B80, 0x3B81, 0xBF80, 0xBB80], dtype=np.uint16)
+    want = np.array([0x3F80, 0x3F82, 0x3F81, 0x0000, 0xBF82], dtype=np.uint16)
+    assert np.array_equal(ln.residual_add(x, r), want)
+
+
+def test_residual_with_zero_residual_is_layernorm():
+    rng = np.random.default_rng(5)
+    x = _rand_bf16(rng, (8, 96), 2.0, 0.5)
+    g = _rand_bf16(rng, (96,), 0.1, 1.0)
+    b = _rand_bf16(rng, (96,), 0.1)
+    h, y, mu, r = ln.layernorm_residual_fwd(x, np.zeros_like(x), g, b, 1e-5)
+    y0, mu0, r0 = ln.layernorm_fwd(x, g, b, 1e-5)
+    assert np.array_equal(h, x) and np.array_equal(y, y0)
+    assert np.array_equal(mu, mu0) and np.array_equal(r, r0)
+    dy = _rand_bf16(rng, (8, 96))
+    dh, dg, db = ln.layernorm_residual_bwd(dy, np.zeros_like(dy), h, g, 1e-5)
+    dx0, dg0, db0 = ln.layernorm_bwd(dy, x, g, 1e-5)
+    assert np.array_equal(dh, dx0) and np.array_equal(dg, dg0) and np.array_equal(db, db0)
+    # with no gradient from the LayerNorm output, dh is the residual gradient itself
+    dres = _rand_bf16(rng, (8, 96), 0.3)
+    dh, dg, db = ln.layernorm_residual_bwd(np.zeros_like(dy), dres, h, g, 1e-5)
+    assert np.array_equal(dh, dres)
+    assert not np.any(to_f64(dg)) and not np.any(to_f64(db))
+
+
+def test_residual_backward_matches_finite_differences():
+    # loss = sum(w * LN(x + r)) + sum(u * (x + r)); both x and r get dh.
+    rng = np.random.default_rng(6)
+    rows, hid, eps = 3, 20, 1e-5
+    x = rng.standard_normal((rows, hid))
+    res = rng.standard_normal((rows, hid))
+    gamma = 1 + 0.1 * rng.standard_normal(hid)
+    beta = 0.1 * rng.standard_normal(hid)
+    w = rng.standard_normal((rows, hid))
+    u = rng.standard_normal((rows, hid))
+    dh, dgamma, dbeta, _ = ln.layernorm_residual_bwd_f64(w, u, x + res, gamma, eps)
+
+    def loss(x_, r_):
+        h_ = x_ + r_
+        return float((ln.layernorm_fwd_f64(h_, gamma, beta, eps)[0] * w).sum() + (h_ * u).sum())
+
+    step = 1e-6
+    for idx in [(0, 0), (1, 9), (2, 19)]:
+        for which in (0, 1):
+            p, m = [x.copy(), res.copy()], [x.copy(), res.copy()]
+            p[which][idx] += step
+            m[which][idx] -= step
+            fd = (loss(*p) - loss(*m)) / (2 * step)
+            assert abs(fd - dh[idx]) < 1e-6 * max(1.0, abs(fd))
