@@ -59,6 +59,9 @@ def bytes_model(sh, n, mb):
     return {
         "layernorm_fwd": rows * hid * 4 + hid * 4 + rows * 8,
         "layernorm_bwd": rows * hid * 6 + hid * 2 + rows * 8 + hid * 4,
+        # fused LayerNorm + residual: reads x, r and writes h, y / reads dy, dres, h and writes dh
+        "layernorm_residual_fwd": rows * hid * 8 + hid * 4 + rows * 8,
+        "layernorm_residual_bwd": rows * hid * 8 + hid * 2 + rows * 8 + hid * 4,
         "alibi_softmax_fwd": live * 2 + full * 2,
         "alibi_softmax_bwd": live * 4 + full * 2,
         "bias_gelu_fwd": grows * gcols * 4 + gcols * 2,
@@ -181,10 +184,34 @@ def run_gpu(args):
         ws = torch.empty(ops.bloom_bias_gelu_bwd_workspace_size(grows, gcols), dtype=torch.uint8, device=dev)
         return lambda: ops.bloom_bias_gelu_bwd(dy, x, ge_b, dx, db, ws)
 
+    def lnr_fwd_set(s):
+        x = fill((rows, hid), W.S_LN_X, 1.0, s=s)
+        res = fill((rows, hid), W.S_LN_RES, 1.0, s=s)
+        h, y = torch.empty_like(x), torch.empty_like(x)
+        m = torch.empty(rows, dtype=f32, device=dev)
+        r = torch.empty_like(m)
+        return lambda: ops.bloom_layernorm_residual_fwd(x, res, ln_g, ln_b, h, y, m, r, W.LN_EPS)
+
+    def lnr_bwd_set(s):
+        h = fill((rows, hid), 53, 1.0, s=s)
+        dy = fill((rows, hid), W.S_LN_DY, 1.0, s=s)
+        dres = fill((rows, hid), W.S_LN_DRES, 1.0, s=s)
+        dh = torch.empty_like(h)
+        m = torch.empty(rows, dtype=f32, device=dev)
+        r = torch.empty_like(m)
+        ops.bloom_layernorm_fwd(h, ln_g, ln_b, dh, m, r, W.LN_EPS)   # saved statistics for the backward
+        dg = torch.empty(hid, dtype=bf, device=dev)
+        db = torch.empty_like(dg)
+        ws = torch.empty(ops.bloom_layernorm_bwd_workspace_size(rows, hid), dtype=torch.uint8, device=dev)
+        return lambda: ops.bloom_layernorm_residual_bwd(dy, dres, h, ln_g, m, r, dh, dg, db, ws)
+
     fused = [("layernorm_fwd", ln_fwd_set, 4), ("alibi_softmax_fwd", sm_fwd_set, 2),
              ("bias_gelu_fwd", ge_fwd_set, 4), ("bias_gelu_bwd", ge_bwd_set, 4),
              ("alibi_softmax_bwd", sm_bwd_set, 2), ("layernorm_bwd", ln_bwd_set, 4)]
     step_fused = [(name, make(0)) for name, make, _ in fused]
+    # Kernels measured in the sweep only (not rows of the step): LayerNorm fused
+    # with the residual connection, at the same [2048, 14336] shape.
+    sweep_only = [("layernorm_residual_fwd", lnr_fwd_set, 4), ("layernorm_residual_bwd", lnr_bwd_set, 4)]
 
     log(f"bench: allocating the shard workload (n = {n:,}, {GRAD_BUFFERS} gradient buffers)")
     master = fill((n,), W.S_OPT_PARAM, W.PARAM_SIGMA, dtype=f32)
@@ -253,8 +280,11 @@ def run_gpu(args):
     # event overhead (a few microseconds) is amortised.
     sweep = {}
     reps = 24
-    for name, make, sets in ([] if args.no_sweep else fused):
-        fns = [step_fused[[nm for nm, _ in step_fused].index(name)][1]] + [make(s) for s in range(1, sets)]
+    for name, make, sets in ([] if args.no_sweep else fused + sweep_only):
+        if name in dict(step_fused):
+            fns = [dict(step_fused)[name]] + [make(s) for s in range(1, sets)]
+        else:
+            fns = [make(s) for s in range(sets)]
         for fn in fns:
             fn()
         torch.cuda.synchronize()
@@ -373,7 +403,7 @@ def main():
                       "timing": "sweep of back-to-back launches on rotating cold inputs" if k in sweep
                       else "events around each launch in the timed steps"}
         if k in sweep:
-            kernels[k]["in_step_ms"] = round(in_step[k], 4)
+            kernels[k]["in_step_ms"] = round(in_step[k], 4) if k in in_step else None
     dom = "grad_accumulate"
     dom_gbs = bts[dom] / (per[dom] * 1e-3) / 1e9
     traffic = measured_traffic(dom)

@@ -53,7 +53,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int bloom_abi_version(void) { return 2; }
+int bloom_abi_version(void) { return 3; }
 
 const char* bloom_status_string(int status) {
   switch (status) {

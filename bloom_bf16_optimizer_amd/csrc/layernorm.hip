@@ -27,9 +27,25 @@ namespace {
 
 constexpr int kGammaLdsMax = 16384;  // widest row whose gamma the backward stages in LDS (32 KiB)
 
-template <int NV, int MAXB>
+// Packed bf16 sum of two vectors: FP32 add, one rounding to nearest even (for
+// bf16 operands the FP32 sum is exact unless the exponents are 16+ apart, and
+// then it lies within 2^-16 of the larger operand, far from a bf16 tie, so the
+// result is the exact sum correctly rounded).
+__device__ __forceinline__ uint4 add_bf16x8(const uint4& a, const uint4& b) {
+  float fa[8], fb[8];
+  unpack8(a, fa);
+  unpack8(b, fb);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) fa[e] += fb[e];
+  return pack8(fa);
+}
+
+// RES: the residual form -- h = bf16(x + res) is formed on load, written to
+// h_out, and normalised in place of x.
+template <int NV, int MAXB, bool RES>
 __global__ __launch_bounds__(MAXB) void ln_fwd_kernel(
-    const uint4* __restrict__ x, const uint4* __restrict__ gamma, const uint4* __restrict__ beta,
+    const uint4* __restrict__ x, const uint4* __restrict__ res, uint4* __restrict__ h_out,
+    const uint4* __restrict__ gamma, const uint4* __restrict__ beta,
     uint4* __restrict__ y, float* __restrict__ mean, float* __restrict__ rstd, int64_t rows,
     int vecs, int tpr, float hidden, float eps) {
   __shared__ float lds[kMaxWaves];
@@ -50,6 +66,20 @@ __global__ __launch_bounds__(MAXB) void ln_fwd_kernel(
   for (int k = 0; k < NV; ++k) {
     const int v = t + k * tpr;
     xv[k] = (v < vecs) ? ld_nt(xr + v) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (RES) {
+    uint4 rv[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int v = t + k * tpr;
+      rv[k] = (v < vecs) ? ld_nt(res + row * vecs + v) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int v = t + k * tpr;
+      xv[k] = add_bf16x8(xv[k], rv[k]);
+      if (v < vecs) st_nt(h_out + row * vecs + v, xv[k]);
+    }
   }
 
   float s = 0.f;
@@ -102,11 +132,14 @@ __global__ __launch_bounds__(MAXB) void ln_fwd_kernel(
 // partial: [gridDim.x][2*H] fp32 -- dgamma partials then dbeta partials.
 // Dynamic LDS: gamma as bf16 (2*H bytes, when H <= kGammaLdsMax), then, in
 // wave mode with several teams, 2*H floats for combining the teams' column sums.
-template <int NV, int MAXB>
+// RES: the residual form -- dres (the gradient reaching x through the
+// residual stream) is added to dx in FP32 before the rounding.
+template <int NV, int MAXB, bool RES>
 __global__ __launch_bounds__(MAXB) void ln_bwd_kernel(
-    const uint4* __restrict__ dy, const uint4* __restrict__ x, const uint4* __restrict__ gamma,
-    const float* __restrict__ mean, const float* __restrict__ rstd, uint4* __restrict__ dx,
-    float* __restrict__ partial, int64_t rows, int vecs, int tpr, float hidden) {
+    const uint4* __restrict__ dy, const uint4* __restrict__ x, const uint4* __restrict__ dres,
+    const uint4* __restrict__ gamma, const float* __restrict__ mean,
+    const float* __restrict__ rstd, uint4* __restrict__ dx, float* __restrict__ partial,
+    int64_t rows, int vecs, int tpr, float hidden) {
   __shared__ float lds[2 * kMaxWaves];
   extern __shared__ uint4 dyn_lds[];
   const bool gamma_staged = vecs * 8 <= kGammaLdsMax;
@@ -170,6 +203,14 @@ __global__ __launch_bounds__(MAXB) void ln_bwd_kernel(
     }
     const float mu = mean[row];
     const float r = rstd[row];
+    uint4 rv[NV];
+    if (RES) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int v = t + k * tpr;
+        rv[k] = (v < vecs) ? ld_nt(dres + row * vecs + v) : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
     // First pass: the row sums of g and g*x_hat, and this row's share of the
     // column sums dgamma += dy*x_hat, dbeta += dy (they need no row statistic).
     float sg = 0.f, sgx = 0.f;
@@ -213,6 +254,12 @@ __global__ __launch_bounds__(MAXB) void ln_bwd_kernel(
         for (int e = 0; e < 8; ++e) {
           const float xh = (f[e] - mu) * r;
           o[e] = r * (d[e] * g[e] - mg - xh * mgx);
+        }
+        if (RES) {
+          float q[8];
+          unpack8(rv[k], q);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] += q[e];
         }
         st_nt(dxr + v, pack8(o));
       }
@@ -265,21 +312,25 @@ __global__ __launch_bounds__(MAXB) void ln_bwd_kernel(
 
 // ---------------------------------------------------------------------------
 // Streaming backward for rows that one workgroup covers exactly (tpr*NV ==
-// vecs, NV <= 2, up to 16 waves): the path of the BLOOM-176B hidden sizes.
+// vecs, NV <= 2): the path of the BLOOM-176B hidden sizes.
 //
 // Each wave streams its own lanes' share of the next two rows straight into
 // LDS with global_load_lds_dwordx4 (16 bytes per lane, written at
 // m0 + lane*16), so two rows are in flight while a third is computed from
-// registers.  A lane only ever reads back the 16-byte slots its own DMA wrote,
-// so the ring needs no barrier: a per-wave s_waitcnt on the vector-memory
-// counter is enough.  The DMA issue and the waits are written as inline
+// registers.  A lane only ever reads back the 16-byte slots its own transfer
+// wrote, so the ring needs no barrier: a per-wave s_waitcnt on the
+// vector-memory counter is enough.  The transfers and the waits are inline
 // assembly with exact counts, because the compiler's own wait insertion
-// drains the whole counter at loop back-edges, which would serialise the
-// rows again.  Every vector-memory instruction a wave issues inside the row
-// loop is accounted for: per row, 2*NV DMA instructions and NV dx stores (the
-// row statistics are scalar loads, counted by lgkmcnt instead).
+// drains the whole counter at loop back-edges, which would serialise the rows
+// again.  Every vector-memory instruction a wave issues in the row loop is
+// accounted for: per row 2*NV row transfers, NV dx stores and, in the
+// residual form, NV transfers of the row's dres (the row statistics are
+// scalar loads, counted by lgkmcnt instead).
 //
-// Ring layout (uint4 units): [slot 2][tensor 2 (dy, x)][k NV][wave 16][lane 64].
+// LDS (dynamic, uint4 units, W = waves of the team):
+//   ring [slot 2][tensor 2 (dy, x)][k NV][wave W][lane 64], then, with RES,
+//   dres [k NV][wave W][lane 64] (one row deep: requested at the start of a
+//   row, read after its reductions).
 // The arithmetic, its order and the partial-row layout are exactly those of
 // ln_bwd_kernel for the same team, so both produce identical bits.
 typedef uint32_t u32x4_lds_t __attribute__((ext_vector_type(4)));
@@ -300,56 +351,57 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Requests `src_row` (a row of `vecs` vectors; or, when !live, a harmless
+// re-read of gamma) for this wave's lanes into LDS at `base`, laid out
+// [k NV][wave W][lane 64].
 template <int NV>
-__device__ __forceinline__ int ring_index(int slot, int q, int k, int w) {
-  return (((slot * 2 + q) * NV + k) * kMaxWaves + w) * kWave;
-}
-
-// Requests row `row` (or, when !live, a harmless re-read of gamma) into `slot`.
-template <int NV>
-__device__ __forceinline__ void ring_issue(lds_uint4* ring, int slot, const uint4* __restrict__ dy,
-                                           const uint4* __restrict__ x, const uint4* __restrict__ gamma,
-                                           int64_t row, bool live, int vecs, int t, int tpr, int w) {
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int v = t + k * tpr;
-      const uint4* src = live ? (q == 0 ? dy : x) + row * vecs + v : gamma + v;
-      dma16(src, __builtin_amdgcn_readfirstlane(lds_offset(ring + ring_index<NV>(slot, q, k, w))));
-    }
-  }
-}
-
-template <int NV>
-__device__ __forceinline__ void ring_read(const lds_uint4* ring, int slot, int w, int lane, uint4 (&d)[NV],
-                                          uint4 (&xv)[NV]) {
-  u32x4_lds_t r[2 * NV];
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const uint32_t a = lds_offset(ring + ring_index<NV>(slot, q, k, w) + lane);
-      asm volatile("ds_read_b128 %0, %1" : "=v"(r[q * NV + k]) : "v"(a) : "memory");
-    }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+__device__ __forceinline__ void lds_issue(lds_uint4* base, const uint4* __restrict__ src_row,
+                                          const uint4* __restrict__ gamma, bool live, int t, int tpr,
+                                          int w, int nwaves) {
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    d[k] = make_uint4(r[k].x, r[k].y, r[k].z, r[k].w);
-    xv[k] = make_uint4(r[NV + k].x, r[NV + k].y, r[NV + k].z, r[NV + k].w);
+    const int v = t + k * tpr;
+    const uint4* src = live ? src_row + v : gamma + v;
+    dma16(src, __builtin_amdgcn_readfirstlane(lds_offset(base + (k * nwaves + w) * kWave)));
   }
 }
 
+// Reads this lane's NV slots.  The reads and their lgkmcnt wait are ONE asm
+// statement: an asm output counts as defined when its statement ends, so a
+// wait in a separate statement would let the compiler schedule uses of the
+// registers before the data has arrived.  Early-clobber outputs keep a
+// destination from sharing a register with an address still to be read.
 template <int NV>
+__device__ __forceinline__ void lds_read(const lds_uint4* base, int w, int lane, int nwaves, uint4 (&out)[NV]) {
+  static_assert(NV == 1 || NV == 2, "lds_read handles one or two slots");
+  u32x4_lds_t r0, r1;
+  const uint32_t a0 = lds_offset(base + (0 * nwaves + w) * kWave + lane);
+  if (NV == 1) {
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r0) : "v"(a0) : "memory");
+  } else {
+    const uint32_t a1 = lds_offset(base + (1 * nwaves + w) * kWave + lane);
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(r0), "=&v"(r1)
+                 : "v"(a0), "v"(a1)
+                 : "memory");
+  }
+  out[0] = make_uint4(r0.x, r0.y, r0.z, r0.w);
+  if (NV == 2) out[NV - 1] = make_uint4(r1.x, r1.y, r1.z, r1.w);
+}
+
+template <int NV, bool RES>
 __global__ __launch_bounds__(kMaxBlock) void ln_bwd_stream_kernel(
-    const uint4* __restrict__ dy, const uint4* __restrict__ x, const uint4* __restrict__ gamma,
-    const float* __restrict__ mean, const float* __restrict__ rstd, uint4* __restrict__ dx,
-    float* __restrict__ partial, int64_t rows, int vecs, float hidden) {
-  __shared__ uint4 ring_storage[2 * 2 * NV * kMaxWaves * kWave];
+    const uint4* __restrict__ dy, const uint4* __restrict__ x, const uint4* __restrict__ dres,
+    const uint4* __restrict__ gamma, const float* __restrict__ mean,
+    const float* __restrict__ rstd, uint4* __restrict__ dx, float* __restrict__ partial,
+    int64_t rows, int vecs, float hidden) {
+  extern __shared__ uint4 stream_lds[];
   __shared__ float red[2][2 * kMaxWaves];
-  lds_uint4* ring = (lds_uint4*)ring_storage;
   const int t = threadIdx.x, tpr = blockDim.x, nwaves = tpr / kWave;
   const int w = t / kWave, lane = t & (kWave - 1);
+  lds_uint4* ring = (lds_uint4*)stream_lds;
+  const int tensor_stride = NV * nwaves * kWave;  // uint4 per [k][wave][lane] block
+  lds_uint4* dres_slot = ring + 4 * tensor_stride;
   const int64_t first = blockIdx.x, stride = gridDim.x;
   const int count = (int)((rows - first + stride - 1) / stride);  // >= 1: grid <= rows
 
@@ -366,26 +418,39 @@ __global__ __launch_bounds__(kMaxBlock) void ln_bwd_stream_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) dg[k][e] = db[k][e] = 0.f;
 
-  ring_issue<NV>(ring, 0, dy, x, gamma, first, true, vecs, t, tpr, w);
-  ring_issue<NV>(ring, 1, dy, x, gamma, first + stride, 1 < count, vecs, t, tpr, w);
+  // slot s, tensor q at ring + (2*s + q) * tensor_stride
+#pragma unroll
+  for (int s0 = 0; s0 < 2; ++s0) {
+    const int64_t row = first + s0 * stride;
+    const bool live = s0 < count;
+    lds_issue<NV>(ring + (2 * s0 + 0) * tensor_stride, dy + row * vecs, gamma, live, t, tpr, w, nwaves);
+    lds_issue<NV>(ring + (2 * s0 + 1) * tensor_stride, x + row * vecs, gamma, live, t, tpr, w, nwaves);
+  }
   for (int i = 0; i < count; ++i) {
     const int slot = i & 1;
     // Row i's transfers are done once no more than the operations issued after
-    // them are outstanding: row 0 -> the transfers of row 1; row 1 -> those of
-    // row 2 and row 0's stores; later -> stores(i-2), transfers(i+1), stores(i-1).
+    // them are outstanding.  Per row: R = dres transfers (NV, residual form
+    // only), T = 2*NV row transfers, S = NV stores.  Row 0: T (row 1's);
+    // row 1: R + T + S of row 0; later: S(i-2) + R + T + S of row i-1.
     if (i >= 2)
-      wait_vmem<4 * NV>();
+      wait_vmem<(RES ? 5 : 4) * NV>();
     else if (i == 1)
-      wait_vmem<3 * NV>();
+      wait_vmem<(RES ? 4 : 3) * NV>();
     else
       wait_vmem<2 * NV>();
     uint4 dv[NV], xv[NV];
-    ring_read<NV>(ring, slot, w, lane, dv, xv);
+    lds_read<NV>(ring + (2 * slot + 0) * tensor_stride, w, lane, nwaves, dv);
+    lds_read<NV>(ring + (2 * slot + 1) * tensor_stride, w, lane, nwaves, xv);
+    const int64_t row = first + (int64_t)i * stride;
+    if (RES) lds_issue<NV>(dres_slot, dres + row * vecs, gamma, true, t, tpr, w, nwaves);
     // The slot is free again: request row i+2 into it (a dummy past the end,
     // so that every iteration issues the same number of operations).
-    ring_issue<NV>(ring, slot, dy, x, gamma, first + (int64_t)(i + 2) * stride, i + 2 < count, vecs, t,
-                   tpr, w);
-    const int64_t row = first + (int64_t)i * stride;
+    {
+      const int64_t nrow = first + (int64_t)(i + 2) * stride;
+      const bool live = i + 2 < count;
+      lds_issue<NV>(ring + (2 * slot + 0) * tensor_stride, dy + nrow * vecs, gamma, live, t, tpr, w, nwaves);
+      lds_issue<NV>(ring + (2 * slot + 1) * tensor_stride, x + nrow * vecs, gamma, live, t, tpr, w, nwaves);
+    }
     const float mu = mean[row];
     const float r = rstd[row];
     float sg = 0.f, sgx = 0.f;
@@ -423,6 +488,11 @@ __global__ __launch_bounds__(kMaxBlock) void ln_bwd_stream_kernel(
     }
     const float mg = a / hidden;
     const float mgx = b / hidden;
+    uint4 qv[NV];
+    if (RES) {
+      wait_vmem<2 * NV>();  // this row's dres: only row i+2's transfers were issued after it
+      lds_read<NV>(dres_slot, w, lane, nwaves, qv);
+    }
     uint4* dxr = dx + row * vecs;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
@@ -434,6 +504,12 @@ __global__ __launch_bounds__(kMaxBlock) void ln_bwd_stream_kernel(
       for (int e = 0; e < 8; ++e) {
         const float xh = (f[e] - mu) * r;
         o[e] = r * (d[e] * gg[e] - mg - xh * mgx);
+      }
+      if (RES) {
+        float q[8];
+        unpack8(qv[k], q);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] += q[e];
       }
       st_nt(dxr + t + k * tpr, pack8(o));
     }
@@ -456,25 +532,33 @@ __global__ __launch_bounds__(kMaxBlock) void ln_bwd_stream_kernel(
   }
 }
 
+constexpr size_t kStreamLdsMax = 160 * 1024 - 2 * 2 * kMaxWaves * sizeof(float);
+
+inline size_t stream_lds_bytes(const RowPlan& p, bool res) {
+  return (size_t)(4 + (res ? 1 : 0)) * p.nv * (p.tpr / kWave) * kWave * sizeof(uint4);
+}
+
 // The streaming backward applies when a block-mode team covers the row with
-// no idle lane and two vectors per thread at most.
-inline bool use_stream_bwd(const RowPlan& p, int vecs) {
-  return p.tpr > kWave && p.block == p.tpr && p.tpr <= kMaxBlock && p.nv <= 2 && p.tpr * p.nv == vecs;
+// no idle lane, at most two vectors per thread, and its ring fits in LDS.
+inline bool use_stream_bwd(const RowPlan& p, int vecs, bool res) {
+  return p.tpr > kWave && p.block == p.tpr && p.tpr <= kMaxBlock && p.nv <= 2 && p.tpr * p.nv == vecs &&
+         stream_lds_bytes(p, res) <= kStreamLdsMax;
 }
 
-template <int NV, int MAXB>
-void launch_fwd(const RowPlan& p, hipStream_t s, const uint4* x, const uint4* g, const uint4* b,
-                uint4* y, float* mean, float* rstd, int64_t rows, int vecs, float eps) {
-  hipLaunchKernelGGL((ln_fwd_kernel<NV, MAXB>), dim3(p.grid), dim3(p.block), 0, s, x, g, b, y, mean, rstd,
-                     rows, vecs, p.tpr, (float)(vecs * 8), eps);
+template <int NV, int MAXB, bool RES>
+void launch_fwd(const RowPlan& p, hipStream_t s, const uint4* x, const uint4* res, uint4* h,
+                const uint4* g, const uint4* b, uint4* y, float* mean, float* rstd, int64_t rows,
+                int vecs, float eps) {
+  hipLaunchKernelGGL((ln_fwd_kernel<NV, MAXB, RES>), dim3(p.grid), dim3(p.block), 0, s, x, res, h, g, b, y,
+                     mean, rstd, rows, vecs, p.tpr, (float)(vecs * 8), eps);
 }
 
-template <int NV, int MAXB>
-void launch_bwd(const RowPlan& p, hipStream_t s, const uint4* dy, const uint4* x, const uint4* g,
-                const float* mean, const float* rstd, uint4* dx, float* partial, int64_t rows,
-                int vecs, size_t lds_bytes) {
-  hipLaunchKernelGGL((ln_bwd_kernel<NV, MAXB>), dim3(p.grid), dim3(p.block), lds_bytes, s, dy, x, g, mean,
-                     rstd, dx, partial, rows, vecs, p.tpr, (float)(vecs * 8));
+template <int NV, int MAXB, bool RES>
+void launch_bwd(const RowPlan& p, hipStream_t s, const uint4* dy, const uint4* x, const uint4* dres,
+                const uint4* g, const float* mean, const float* rstd, uint4* dx, float* partial,
+                int64_t rows, int vecs, size_t lds_bytes) {
+  hipLaunchKernelGGL((ln_bwd_kernel<NV, MAXB, RES>), dim3(p.grid), dim3(p.block), lds_bytes, s, dy, x, dres, g,
+                     mean, rstd, dx, partial, rows, vecs, p.tpr, (float)(vecs * 8));
 }
 
 bloom_status check_rows(int64_t rows, int64_t hidden) {
@@ -484,6 +568,91 @@ bloom_status check_rows(int64_t rows, int64_t hidden) {
                 BLOOM_MAX_HIDDEN);
   BLOOM_REQUIRE(rows <= (int64_t(1) << 40) / hidden, BLOOM_ERR_SHAPE, "rows*hidden too large");
   return BLOOM_OK;
+}
+
+// Shared by the plain and the residual forward (res == NULL: plain).
+template <bool RES>
+bloom_status layernorm_fwd_impl(const char* name, const bloom_bf16* x, const bloom_bf16* res,
+                                bloom_bf16* h, const bloom_bf16* gamma, const bloom_bf16* beta,
+                                bloom_bf16* y, float* mean, float* rstd, int64_t rows, int64_t hidden,
+                                float eps, hipStream_t stream) {
+  if (bloom_status st = check_rows(rows, hidden)) return st;
+  BLOOM_REQUIRE(eps > 0.f && eps < INFINITY, BLOOM_ERR_HPARAM, "eps must be positive and finite");
+  if (rows == 0) return BLOOM_OK;
+  BLOOM_REQUIRE_PTR(x);
+  if (RES) {
+    BLOOM_REQUIRE_PTR(res);
+    BLOOM_REQUIRE_PTR(h);
+  }
+  BLOOM_REQUIRE_PTR(gamma);
+  BLOOM_REQUIRE_PTR(beta);
+  BLOOM_REQUIRE_PTR(y);
+  BLOOM_REQUIRE_PTR(mean);
+  BLOOM_REQUIRE_PTR(rstd);
+  const int vecs = (int)(hidden / 8);
+  const RowPlan p = plan_rows_fwd(rows, vecs);
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const uint4* rv = reinterpret_cast<const uint4*>(res);
+  uint4* hv = reinterpret_cast<uint4*>(h);
+  const uint4* gv = reinterpret_cast<const uint4*>(gamma);
+  const uint4* bv = reinterpret_cast<const uint4*>(beta);
+  uint4* yv = reinterpret_cast<uint4*>(y);
+#define CALL(NV, MAXB) launch_fwd<NV, MAXB, RES>(p, stream, xv, rv, hv, gv, bv, yv, mean, rstd, rows, vecs, eps)
+  BLOOM_ROW_DISPATCH(p, CALL);
+#undef CALL
+  return launch_status(name);
+}
+
+// Shared by the plain and the residual backward (dres == NULL: plain).
+template <bool RES>
+bloom_status layernorm_bwd_impl(const char* name, const bloom_bf16* dy, const bloom_bf16* x,
+                                const bloom_bf16* dres, const bloom_bf16* gamma, const float* mean,
+                                const float* rstd, bloom_bf16* dx, bloom_bf16* dgamma, bloom_bf16* dbeta,
+                                void* workspace, size_t workspace_bytes, int64_t rows, int64_t hidden,
+                                hipStream_t stream) {
+  if (bloom_status st = check_rows(rows, hidden)) return st;
+  if (rows == 0) return BLOOM_OK;
+  BLOOM_REQUIRE_PTR(dy);
+  BLOOM_REQUIRE_PTR(x);
+  if (RES) BLOOM_REQUIRE_PTR(dres);
+  BLOOM_REQUIRE_PTR(gamma);
+  BLOOM_REQUIRE_PTR(mean);
+  BLOOM_REQUIRE_PTR(rstd);
+  BLOOM_REQUIRE_PTR(dx);
+  BLOOM_REQUIRE_PTR(dgamma);
+  BLOOM_REQUIRE_PTR(dbeta);
+  BLOOM_REQUIRE(workspace != nullptr, BLOOM_ERR_WORKSPACE, "workspace is NULL");
+  BLOOM_REQUIRE(aligned16(workspace), BLOOM_ERR_ALIGN, "workspace is not 16-byte aligned");
+  const int vecs = (int)(hidden / 8);
+  const RowPlan p = plan_rows_bwd(rows, vecs, device_cu_count());
+  const size_t need = (size_t)p.grid * 2 * (size_t)hidden * sizeof(float);
+  BLOOM_REQUIRE(workspace_bytes >= need, BLOOM_ERR_WORKSPACE,
+                "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  float* partial = static_cast<float*>(workspace);
+  const uint4* dyv = reinterpret_cast<const uint4*>(dy);
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const uint4* rv = reinterpret_cast<const uint4*>(dres);
+  const uint4* gv = reinterpret_cast<const uint4*>(gamma);
+  uint4* dxv = reinterpret_cast<uint4*>(dx);
+  if (use_stream_bwd(p, vecs, RES)) {
+    const size_t lds = stream_lds_bytes(p, RES);
+    if (p.nv == 1)
+      hipLaunchKernelGGL((ln_bwd_stream_kernel<1, RES>), dim3(p.grid), dim3(p.block), lds, stream, dyv, xv, rv,
+                         gv, mean, rstd, dxv, partial, rows, vecs, (float)hidden);
+    else
+      hipLaunchKernelGGL((ln_bwd_stream_kernel<2, RES>), dim3(p.grid), dim3(p.block), lds, stream, dyv, xv, rv,
+                         gv, mean, rstd, dxv, partial, rows, vecs, (float)hidden);
+  } else {
+    const size_t lds = (hidden <= kGammaLdsMax ? 2 * (size_t)hidden : 0) +
+                       ((p.tpr == kWave && p.block > kWave) ? 2 * (size_t)hidden * sizeof(float) : 0);
+#define CALL(NV, MAXB) \
+  launch_bwd<NV, MAXB, RES>(p, stream, dyv, xv, rv, gv, mean, rstd, dxv, partial, rows, vecs, lds)
+    BLOOM_ROW_DISPATCH(p, CALL);
+#undef CALL
+  }
+  if (bloom_status st = launch_status(name)) return st;
+  launch_colsum(partial, p.grid, 2 * hidden, hidden, dgamma, dbeta, stream);
+  return launch_status(name);
 }
 
 }  // namespace
@@ -496,25 +665,18 @@ extern "C" bloom_status bloom_layernorm_fwd(const bloom_bf16* x, const bloom_bf1
                                             float* rstd, int64_t rows, int64_t hidden, float eps,
                                             hipStream_t stream) {
   clear_error();
-  if (bloom_status st = check_rows(rows, hidden)) return st;
-  BLOOM_REQUIRE(eps > 0.f && eps < INFINITY, BLOOM_ERR_HPARAM, "eps must be positive and finite");
-  if (rows == 0) return BLOOM_OK;
-  BLOOM_REQUIRE_PTR(x);
-  BLOOM_REQUIRE_PTR(gamma);
-  BLOOM_REQUIRE_PTR(beta);
-  BLOOM_REQUIRE_PTR(y);
-  BLOOM_REQUIRE_PTR(mean);
-  BLOOM_REQUIRE_PTR(rstd);
-  const int vecs = (int)(hidden / 8);
-  const RowPlan p = plan_rows_fwd(rows, vecs);
-  const uint4* xv = reinterpret_cast<const uint4*>(x);
-  const uint4* gv = reinterpret_cast<const uint4*>(gamma);
-  const uint4* bv = reinterpret_cast<const uint4*>(beta);
-  uint4* yv = reinterpret_cast<uint4*>(y);
-#define CALL(NV, MAXB) launch_fwd<NV, MAXB>(p, stream, xv, gv, bv, yv, mean, rstd, rows, vecs, eps)
-  BLOOM_ROW_DISPATCH(p, CALL);
-#undef CALL
-  return launch_status("bloom_layernorm_fwd");
+  return layernorm_fwd_impl<false>("bloom_layernorm_fwd", x, nullptr, nullptr, gamma, beta, y, mean, rstd,
+                                   rows, hidden, eps, stream);
+}
+
+extern "C" bloom_status bloom_layernorm_residual_fwd(const bloom_bf16* x, const bloom_bf16* residual,
+                                                     const bloom_bf16* gamma, const bloom_bf16* beta,
+                                                     bloom_bf16* h, bloom_bf16* y, float* mean,
+                                                     float* rstd, int64_t rows, int64_t hidden, float eps,
+                                                     hipStream_t stream) {
+  clear_error();
+  return layernorm_fwd_impl<true>("bloom_layernorm_residual_fwd", x, residual, h, gamma, beta, y, mean,
+                                  rstd, rows, hidden, eps, stream);
 }
 
 extern "C" size_t bloom_layernorm_bwd_workspace_size(int64_t rows, int64_t hidden) {
@@ -530,44 +692,18 @@ extern "C" bloom_status bloom_layernorm_bwd(const bloom_bf16* dy, const bloom_bf
                                             size_t workspace_bytes, int64_t rows, int64_t hidden,
                                             hipStream_t stream) {
   clear_error();
-  if (bloom_status st = check_rows(rows, hidden)) return st;
-  if (rows == 0) return BLOOM_OK;
-  BLOOM_REQUIRE_PTR(dy);
-  BLOOM_REQUIRE_PTR(x);
-  BLOOM_REQUIRE_PTR(gamma);
-  BLOOM_REQUIRE_PTR(mean);
-  BLOOM_REQUIRE_PTR(rstd);
-  BLOOM_REQUIRE_PTR(dx);
-  BLOOM_REQUIRE_PTR(dgamma);
-  BLOOM_REQUIRE_PTR(dbeta);
-  BLOOM_REQUIRE(workspace != nullptr, BLOOM_ERR_WORKSPACE, "workspace is NULL");
-  BLOOM_REQUIRE(aligned16(workspace), BLOOM_ERR_ALIGN, "workspace is not 16-byte aligned");
-  const int vecs = (int)(hidden / 8);
-  const RowPlan p = plan_rows_bwd(rows, vecs, device_cu_count());
-  const size_t need = (size_t)p.grid * 2 * (size_t)hidden * sizeof(float);
-  BLOOM_REQUIRE(workspace_bytes >= need, BLOOM_ERR_WORKSPACE,
-                "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-  float* partial = static_cast<float*>(workspace);
-  const size_t lds = (hidden <= kGammaLdsMax ? 2 * (size_t)hidden : 0) +
-                     ((p.tpr == kWave && p.block > kWave) ? 2 * (size_t)hidden * sizeof(float) : 0);
-  const uint4* dyv = reinterpret_cast<const uint4*>(dy);
-  const uint4* xv = reinterpret_cast<const uint4*>(x);
-  const uint4* gv = reinterpret_cast<const uint4*>(gamma);
-  uint4* dxv = reinterpret_cast<uint4*>(dx);
-  if (use_stream_bwd(p, vecs)) {
-    if (p.nv == 1)
-      hipLaunchKernelGGL((ln_bwd_stream_kernel<1>), dim3(p.grid), dim3(p.block), 0, stream, dyv, xv, gv, mean,
-                         rstd, dxv, partial, rows, vecs, (float)hidden);
-    else
-      hipLaunchKernelGGL((ln_bwd_stream_kernel<2>), dim3(p.grid), dim3(p.block), 0, stream, dyv, xv, gv, mean,
-                         rstd, dxv, partial, rows, vecs, (float)hidden);
-  } else {
-#define CALL(NV, MAXB) \
-  launch_bwd<NV, MAXB>(p, stream, dyv, xv, gv, mean, rstd, dxv, partial, rows, vecs, lds)
-    BLOOM_ROW_DISPATCH(p, CALL);
-#undef CALL
-  }
-  if (bloom_status st = launch_status("bloom_layernorm_bwd")) return st;
-  launch_colsum(partial, p.grid, 2 * hidden, hidden, dgamma, dbeta, stream);
-  return launch_status("bloom_layernorm_bwd column sums");
+  return layernorm_bwd_impl<false>("bloom_layernorm_bwd", dy, x, nullptr, gamma, mean, rstd, dx, dgamma,
+                                   dbeta, workspace, workspace_bytes, rows, hidden, stream);
+}
+
+extern "C" bloom_status bloom_layernorm_residual_bwd(const bloom_bf16* dy, const bloom_bf16* dres,
+                                                     const bloom_bf16* h, const bloom_bf16* gamma,
+                                                     const float* mean, const float* rstd,
+                                                     bloom_bf16* dh, bloom_bf16* dgamma,
+                                                     bloom_bf16* dbeta, void* workspace,
+                                                     size_t workspace_bytes, int64_t rows,
+                                                     int64_t hidden, hipStream_t stream) {
+  clear_error();
+  return layernorm_bwd_impl<true>("bloom_layernorm_residual_bwd", dy, h, dres, gamma, mean, rstd, dh,
+                                  dgamma, dbeta, workspace, workspace_bytes, rows, hidden, stream);
 }

@@ -90,6 +90,36 @@ def bloom_layernorm_bwd(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace) 
         _stream()))
 
 
+def bloom_layernorm_residual_fwd(x, residual, gamma, beta, h, y, mean, rstd, eps: float) -> None:
+    rows, hidden = _rows_cols(x)
+    for t, name in ((residual, "residual"), (h, "h"), (y, "y")):
+        _same(x, t, f"x/{name}")
+    if gamma.numel() != hidden or beta.numel() != hidden or mean.numel() != rows or rstd.numel() != rows:
+        raise ValueError("gamma/beta must have `hidden` and mean/rstd `rows` elements")
+    lib = _lib.load()
+    check("bloom_layernorm_residual_fwd", lib.bloom_layernorm_residual_fwd(
+        _ptr(x, BF16, "x"), _ptr(residual, BF16, "residual"), _ptr(gamma, BF16, "gamma"),
+        _ptr(beta, BF16, "beta"), _ptr(h, BF16, "h"), _ptr(y, BF16, "y"), _ptr(mean, F32, "mean"),
+        _ptr(rstd, F32, "rstd"), rows, hidden, eps, _stream()))
+
+
+def bloom_layernorm_residual_bwd(dy, dres, h, gamma, mean, rstd, dh, dgamma, dbeta, workspace) -> None:
+    rows, hidden = _rows_cols(h)
+    for t, name in ((dy, "dy"), (dres, "dres"), (dh, "dh")):
+        _same(h, t, f"h/{name}")
+    if gamma.numel() != hidden or dgamma.numel() != hidden or dbeta.numel() != hidden:
+        raise ValueError("gamma/dgamma/dbeta must have `hidden` elements")
+    if mean.numel() != rows or rstd.numel() != rows:
+        raise ValueError("mean/rstd must have `rows` elements")
+    wsb = workspace.numel() * workspace.element_size()
+    lib = _lib.load()
+    check("bloom_layernorm_residual_bwd", lib.bloom_layernorm_residual_bwd(
+        _ptr(dy, BF16, "dy"), _ptr(dres, BF16, "dres"), _ptr(h, BF16, "h"), _ptr(gamma, BF16, "gamma"),
+        _ptr(mean, F32, "mean"), _ptr(rstd, F32, "rstd"), _ptr(dh, BF16, "dh"), _ptr(dgamma, BF16, "dgamma"),
+        _ptr(dbeta, BF16, "dbeta"), _ptr(workspace, workspace.dtype, "workspace"), wsb, rows, hidden,
+        _stream()))
+
+
 def _softmax_shape(t: torch.Tensor):
     if t.dim() != 4 or t.shape[2] != t.shape[3]:
         raise ValueError("scores must be [batch, heads, seq, seq]")

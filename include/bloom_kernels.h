@@ -103,6 +103,38 @@ bloom_status bloom_layernorm_bwd(const bloom_bf16* dy, const bloom_bf16* x,
                                  bloom_bf16* dbeta, void* workspace, size_t workspace_bytes,
                                  int64_t rows, int64_t hidden, hipStream_t stream);
 
+/* LayerNorm fused with the residual connection, forward.  [3d] 4.3 (a fused
+ * LayerNorm + residual kernel, printed there as a stub); the LayerNorm is the
+ * one of bloom_layernorm_fwd.  BLOOM's blocks are pre-LN, so the sum is also
+ * the residual stream the next block adds to, and it is written out:
+ *   h = x + residual, added in FP32 and rounded once to bf16 (for bf16
+ *       inputs this is the exact sum rounded to nearest even)
+ *   y = LayerNorm(h), bit for bit what bloom_layernorm_fwd returns for h.
+ * x, residual, h, y [rows, hidden] bf16; gamma, beta [hidden] bf16;
+ * mean, rstd [rows] fp32 of h.  h must not overlap x or residual.
+ */
+bloom_status bloom_layernorm_residual_fwd(const bloom_bf16* x, const bloom_bf16* residual,
+                                          const bloom_bf16* gamma, const bloom_bf16* beta,
+                                          bloom_bf16* h, bloom_bf16* y, float* mean, float* rstd,
+                                          int64_t rows, int64_t hidden, float eps,
+                                          hipStream_t stream);
+
+/* Backward of bloom_layernorm_residual_fwd.  [3d] 4.3.
+ *   dh = dLN(dy; h) + dres, summed in FP32 and rounded once, where dLN is
+ *        the dx of bloom_layernorm_bwd with x = h and dres is the gradient
+ *        reaching h through the residual stream; dh is the gradient of both
+ *        x and residual
+ *   dgamma, dbeta as bloom_layernorm_bwd on h.
+ * dy, dres, h, dh [rows, hidden] bf16; gamma [hidden]; mean, rstd [rows] fp32
+ * from the forward; workspace as for bloom_layernorm_bwd (same size query).
+ */
+bloom_status bloom_layernorm_residual_bwd(const bloom_bf16* dy, const bloom_bf16* dres,
+                                          const bloom_bf16* h, const bloom_bf16* gamma,
+                                          const float* mean, const float* rstd, bloom_bf16* dh,
+                                          bloom_bf16* dgamma, bloom_bf16* dbeta, void* workspace,
+                                          size_t workspace_bytes, int64_t rows, int64_t hidden,
+                                          hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * ALiBi slopes (host only, no device work).  [overview] "架构微调" (ALiBi
  * replaces position embeddings) and "资源" (the ALiBi paper, arXiv:2108.12409,

@@ -37,7 +37,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for required in ["bloom_layernorm_fwd", "bloom_layernorm_bwd", "bloom_alibi_softmax_fwd",
+    for required in ["bloom_layernorm_fwd", "bloom_layernorm_bwd", "bloom_layernorm_residual_fwd",
+                     "bloom_layernorm_residual_bwd", "bloom_alibi_softmax_fwd",
                      "bloom_alibi_softmax_bwd", "bloom_bias_gelu_fwd", "bloom_bias_gelu_bwd",
                      "bloom_bf16_grad_accumulate", "bloom_bf16_adamw_step", "bloom_alibi_slopes"]:
         assert required in names
@@ -50,7 +51,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.bloom_abi_version() == 2
+    assert lib.bloom_abi_version() == 3
     assert lib.bloom_status_string(0) == b"ok"
     assert lib.bloom_status_string(4) == b"workspace too small"
     assert lib.bloom_status_string(99) == b"unknown status"
@@ -95,6 +96,22 @@ def test_layernorm_validation(lib):
     assert b(p, p, p, p, p, p, p, p, p, 16, 4, 16, None) == WORKSPACE
     assert b(p, p, p, p, p, p, p, p, p + 4, 1 << 20, 4, 16, None) == ALIGN
     assert lib.bloom_layernorm_bwd_workspace_size(4, 12) == 0
+
+
+def test_layernorm_residual_validation(lib):
+    p = FAKE
+    f = lib.bloom_layernorm_residual_fwd
+    assert f(p, p, p, p, p, p, p, p, 4, 12, 1e-5, None) == SHAPE
+    assert f(p, p, p, p, p, p, p, p, 4, 16, -1.0, None) == HPARAM
+    assert f(p, None, p, p, p, p, p, p, 4, 16, 1e-5, None) == NULL
+    assert f(p, p, p, p, None, p, p, p, 4, 16, 1e-5, None) == NULL
+    assert f(p, p, p, p, p + 8, p, p, p, 4, 16, 1e-5, None) == ALIGN
+    assert f(p, p, p, p, p, p, p, p, 0, 16, 1e-5, None) == OK
+    b = lib.bloom_layernorm_residual_bwd
+    ws = lib.bloom_layernorm_bwd_workspace_size(4, 16)
+    assert b(p, None, p, p, p, p, p, p, p, p, ws, 4, 16, None) == NULL
+    assert b(p, p, p, p, p, p, p, p, p, p, ws - 16, 4, 16, None) == WORKSPACE
+    assert b(p, p, p, p, p, p, p, p, p, p, ws, 0, 16, None) == OK
 
 
 def test_softmax_validation(lib):
