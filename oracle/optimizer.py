@@ -29,6 +29,19 @@ Readings where the pages are silent:
   evaluated in float64 from the float32 state and the float64 hyperparameters,
   then rounded once to float32;
 * bf16 parameter copy: round-to-nearest-even of the float32 master.
+
+Parameter groups and schedule (the "optimizer group splitting" named among the
+engineering challenges on page "BLOOM 176B 训练技术概览"; page
+"单机多卡实战：Megatron-DeepSpeed训练类BLOOM模型全流程解析", section 3's config:
+lr 6e-5, min_lr 1e-6, cosine decay, 500 warmup iterations, 100000 train
+iterations).  Readings:
+
+* groups are contiguous segments of the flat buffers, each with its own
+  weight decay (e.g. none on biases and LayerNorm weights); the norm and the
+  clip coefficient stay global over all segments;
+* lr at optimizer step t (1-based): t * max_lr / warmup while t <= warmup;
+  then min_lr + (max_lr - min_lr) * (1 + cos(pi * (t - warmup) /
+  (decay - warmup))) / 2 up to t = decay (the train iterations); min_lr after.
 """
 
 from __future__ import annotations
@@ -110,3 +123,31 @@ def bf16_optimizer_step(master, m, v, acc, lr: float, beta1: float, beta2: float
     c = clip_coefficient(norm, max_grad_norm)
     p1, m1, v1, pb = adamw_update(master, m, v, acc, c, lr, beta1, beta2, eps, weight_decay, step)
     return p1, m1, v1, pb, norm, c
+
+
+def bf16_optimizer_step_segments(master, m, v, acc, segments, lr: float, beta1: float, beta2: float,
+                                 eps: float, max_grad_norm: float, step: int):
+    """Global norm and clip over all of acc, then AdamW per segment (offset, length, weight_decay).
+
+    Returns (master', m', v', param bf16 bits, N, c).
+    """
+    norm = global_norm(acc)
+    c = clip_coefficient(norm, max_grad_norm)
+    p1 = np.empty(len(acc), dtype=np.float32)
+    m1, v1 = np.empty_like(p1), np.empty_like(p1)
+    pb = np.empty(len(acc), dtype=np.uint16)
+    for off, length, wd in segments:
+        sl = slice(off, off + length)
+        p1[sl], m1[sl], v1[sl], pb[sl] = adamw_update(master[sl], m[sl], v[sl], acc[sl], c, lr, beta1, beta2,
+                                                      eps, wd, step)
+    return p1, m1, v1, pb, norm, c
+
+
+def lr_warmup_cosine(step: int, max_lr: float, min_lr: float, warmup: int, decay: int) -> float:
+    """Learning rate at optimizer step ``step`` (1-based), float64."""
+    if warmup > 0 and step <= warmup:
+        return max_lr * step / warmup
+    if step >= decay:
+        return min_lr
+    ratio = (step - warmup) / (decay - warmup)
+    return min_lr + (max_lr - min_lr) * 0.5 * (1.0 + np.cos(np.pi * ratio))

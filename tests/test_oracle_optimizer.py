@@ -127,3 +127,72 @@ def test_first_step_invariants():
     assert np.array_equal(p1, p64.astype(np.float32)) and np.array_equal(m1, m64.astype(np.float32))
     t = torch.from_numpy(p1).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(pb, t)
+
+
+def test_segments_match_torch_adamw_param_groups():
+    """Weight-decay segments with one global clip, against torch's AdamW with
+    two parameter groups and the norm over both groups (float64)."""
+    rng = np.random.default_rng(17)
+    n, cut = 3000, 1800                   # [0, 1800): wd 0.01; [1800, 3000): wd 0 (biases, LayerNorm)
+    p = (0.02 * rng.standard_normal(n)).astype(np.float32)
+    m = (1e-4 * rng.standard_normal(n)).astype(np.float32)
+    v = np.abs(1e-6 * rng.standard_normal(n)).astype(np.float32)
+    acc = (0.05 * rng.standard_normal(n)).astype(np.float32)
+    lr, b1, b2, eps, step = 6e-5, 0.9, 0.999, 1e-8, 3
+    segs = [(0, cut, 0.01), (cut, n - cut, 0.0)]
+    p1, m1, v1, pb, norm, c = opt.bf16_optimizer_step_segments(p, m, v, acc, segs, lr, b1, b2, eps, 1.0, step)
+    assert c < 1.0
+
+    groups = [torch.nn.Parameter(torch.from_numpy(p[:cut].astype(np.float64))),
+              torch.nn.Parameter(torch.from_numpy(p[cut:].astype(np.float64)))]
+    o = torch.optim.AdamW([{"params": [groups[0]], "weight_decay": 0.01},
+                           {"params": [groups[1]], "weight_decay": 0.0}],
+                          lr=lr, betas=(b1, b2), eps=eps, foreach=False)
+    for tp, sl in zip(groups, (slice(0, cut), slice(cut, n))):
+        tp.grad = torch.from_numpy(acc[sl].astype(np.float64))
+        st = o.state[tp]
+        st["step"] = torch.tensor(float(step - 1), dtype=torch.float64)
+        st["exp_avg"] = torch.from_numpy(m[sl].astype(np.float64))
+        st["exp_avg_sq"] = torch.from_numpy(v[sl].astype(np.float64))
+    # the global norm over both groups from torch (max_norm = inf: measure only; torch's own clip
+    # divides by N + 1e-6, so the gradients are scaled by max_norm / N here instead)
+    tn = torch.nn.utils.clip_grad_norm_(groups, max_norm=float("inf"))
+    assert abs(tn.item() - norm) < 1e-12 * norm
+    for tp in groups:
+        tp.grad.mul_(1.0 / tn)
+    o.step()
+    tp_all = np.concatenate([g.detach().numpy() for g in groups])
+    # float32 results vs the float64 library: within one float32 rounding
+    assert np.all(np.abs(tp_all - p1) <= np.abs(tp_all) * 2.0 ** -23 + 1e-30)
+    # the undecayed segment moved by the Adam term only: p1 differs from a decayed update there
+    _, _, _, pb_decayed, _, _ = opt.bf16_optimizer_step(p, m, v, acc, lr, b1, b2, eps, 0.01, 1.0, step)
+    assert np.array_equal(pb[:cut], pb_decayed[:cut])
+
+
+def test_single_segment_is_the_plain_step():
+    rng = np.random.default_rng(18)
+    n = 777
+    p = (0.02 * rng.standard_normal(n)).astype(np.float32)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    acc = (0.5 * rng.standard_normal(n)).astype(np.float32)
+    a = opt.bf16_optimizer_step(p, m, v, acc, 6e-5, 0.9, 0.999, 1e-8, 0.01, 1.0, 1)
+    b = opt.bf16_optimizer_step_segments(p, m, v, acc, [(0, n, 0.01)], 6e-5, 0.9, 0.999, 1e-8, 1.0, 1)
+    for x, y in zip(a[:4], b[:4]):
+        assert np.array_equal(x, y)
+    assert a[4:] == b[4:]
+
+
+def test_lr_schedule_closed_forms():
+    """The page's schedule (lr 6e-5, min 1e-6, 500 warmup, 100000 iterations)
+    at points where cos takes exact values."""
+    f = lambda t: opt.lr_warmup_cosine(t, 6e-5, 1e-6, 500, 100000)
+    assert f(1) == 6e-5 / 500 and f(250) == 3e-5 and f(500) == 6e-5
+    assert abs(f(50250) - (6e-5 + 1e-6) / 2) < 1e-20          # cos(pi/2) = 0
+    quarter = 500 + (100000 - 500) // 4                        # (t - W)/(D - W) = 1/4 exactly? 99500/4 = 24875
+    assert abs(f(quarter) - (1e-6 + (6e-5 - 1e-6) * (1 + np.sqrt(0.5)) / 2)) < 1e-18
+    assert f(100000) == 1e-6 and f(250000) == 1e-6
+    ts = np.arange(500, 100001, 997)
+    lrs = np.array([f(int(t)) for t in ts])
+    assert np.all(np.diff(lrs) < 0)                            # decays monotonically
+    assert opt.lr_warmup_cosine(3, 1.0, 0.0, 0, 10) == (1 + np.cos(np.pi * 0.3)) / 2   # no warmup
