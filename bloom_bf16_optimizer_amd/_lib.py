@@ -29,6 +29,10 @@ class AdamWHParams(ctypes.Structure):
                 ("sumsq_in_workspace", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class AdamWSegment(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_int64), ("length", ctypes.c_int64), ("weight_decay", ctypes.c_double)]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "bloom_abi_version": (ctypes.c_int, []),
@@ -53,6 +57,11 @@ SIGNATURES = {
                                                         c_void_p]),
     "bloom_bf16_adamw_step": (ctypes.c_int, [c_void_p] * 5 + [c_i64, ctypes.POINTER(AdamWHParams), c_void_p,
                                              c_void_p, c_size, c_void_p]),
+    "bloom_bf16_adamw_step_segments": (ctypes.c_int, [c_void_p] * 5 + [c_i64, ctypes.POINTER(AdamWHParams),
+                                                      ctypes.POINTER(AdamWSegment), c_i32, c_void_p,
+                                                      c_void_p, c_size, c_void_p]),
+    "bloom_lr_warmup_cosine": (ctypes.c_int, [c_i64, ctypes.c_double, ctypes.c_double, c_i64, c_i64,
+                                              ctypes.POINTER(ctypes.c_double)]),
 }
 
 _lib = None

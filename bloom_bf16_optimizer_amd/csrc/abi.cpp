@@ -1,7 +1,9 @@
 // ABI plumbing: version, status strings, the thread-local error message, the
-// launch check and the cached device query.  Also the host-only ALiBi slope
-// table (the slope rule of the ALiBi paper, arXiv:2108.12409, cited by page
-// "BLOOM 176B 训练技术概览" under "资源" for the bias of "架构微调").
+// launch check and the cached device query.  Also two host-only functions:
+// the ALiBi slope table (the slope rule of the ALiBi paper, arXiv:2108.12409,
+// cited by page "BLOOM 176B 训练技术概览" under "资源" for the bias of
+// "架构微调") and the warmup + cosine learning-rate schedule of section 3's
+// training config on page "单机多卡实战：Megatron-DeepSpeed训练类BLOOM模型全流程解析".
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -53,7 +55,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int bloom_abi_version(void) { return 3; }
+int bloom_abi_version(void) { return 4; }
 
 const char* bloom_status_string(int status) {
   switch (status) {
@@ -97,3 +99,24 @@ bloom_status bloom_alibi_slopes(int32_t total_heads, int32_t head_offset, int32_
 }
 
 }  // extern "C"
+
+extern "C" bloom_status bloom_lr_warmup_cosine(int64_t step, double max_lr, double min_lr,
+                                               int64_t warmup_steps, int64_t decay_steps, double* lr_out) {
+  bloom::clear_error();
+  if (lr_out == nullptr) return bloom::fail(BLOOM_ERR_NULL, "lr_out is NULL");
+  if (step < 1) return bloom::fail(BLOOM_ERR_HPARAM, "step = %lld must be >= 1", (long long)step);
+  if (!(std::isfinite(max_lr) && std::isfinite(min_lr) && min_lr >= 0.0 && min_lr <= max_lr))
+    return bloom::fail(BLOOM_ERR_HPARAM, "need 0 <= min_lr <= max_lr, both finite");
+  if (warmup_steps < 0 || decay_steps <= warmup_steps)
+    return bloom::fail(BLOOM_ERR_HPARAM, "need 0 <= warmup_steps < decay_steps");
+  const double pi = 3.14159265358979323846;
+  if (warmup_steps > 0 && step <= warmup_steps) {
+    *lr_out = max_lr * (double)step / (double)warmup_steps;
+  } else if (step >= decay_steps) {
+    *lr_out = min_lr;
+  } else {
+    const double q = (double)(step - warmup_steps) / (double)(decay_steps - warmup_steps);
+    *lr_out = min_lr + (max_lr - min_lr) * 0.5 * (1.0 + std::cos(pi * q));
+  }
+  return BLOOM_OK;
+}

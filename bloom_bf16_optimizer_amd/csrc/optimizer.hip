@@ -310,12 +310,16 @@ extern "C" bloom_status bloom_bf16_grad_accumulate_sumsq(float* grad_acc, const 
   return launch_accumulate(grad_acc, grad, n, first_microbatch, partial, stream);
 }
 
-extern "C" bloom_status bloom_bf16_adamw_step(float* master, float* exp_avg, float* exp_avg_sq,
-                                              bloom_bf16* param_bf16, const float* grad_acc,
-                                              int64_t n, const bloom_adamw_hparams* hp,
-                                              float* grad_norm_out, void* workspace,
-                                              size_t workspace_bytes, hipStream_t stream) {
-  clear_error();
+namespace bloom {
+namespace {
+
+// Shared by the flat and the segmented step: validation, norm, clip, then one
+// AdamW launch per segment with that segment's decay.
+bloom_status adamw_step_impl(const char* name, float* master, float* exp_avg, float* exp_avg_sq,
+                             bloom_bf16* param_bf16, const float* grad_acc, int64_t n,
+                             const bloom_adamw_hparams* hp, const bloom_adamw_segment* segments,
+                             int32_t num_segments, float* grad_norm_out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
   BLOOM_REQUIRE(n >= 0 && n <= kMaxElems, BLOOM_ERR_SHAPE, "n = %lld out of range", (long long)n);
   BLOOM_REQUIRE(hp != nullptr, BLOOM_ERR_NULL, "hp is NULL");
   BLOOM_REQUIRE(finite_nonneg(hp->lr), BLOOM_ERR_HPARAM, "lr must be finite and >= 0");
@@ -323,13 +327,27 @@ extern "C" bloom_status bloom_bf16_adamw_step(float* master, float* exp_avg, flo
   BLOOM_REQUIRE(hp->beta2 >= 0.0 && hp->beta2 < 1.0, BLOOM_ERR_HPARAM, "beta2 must be in [0, 1)");
   BLOOM_REQUIRE(std::isfinite(hp->eps) && hp->eps > 0.0, BLOOM_ERR_HPARAM,
                 "eps must be finite and > 0");
-  BLOOM_REQUIRE(finite_nonneg(hp->weight_decay), BLOOM_ERR_HPARAM,
-                "weight_decay must be finite and >= 0");
   BLOOM_REQUIRE(hp->max_grad_norm > 0.0, BLOOM_ERR_HPARAM, "max_grad_norm must be > 0");
   BLOOM_REQUIRE(hp->step >= 1, BLOOM_ERR_HPARAM, "step must be >= 1");
   BLOOM_REQUIRE(hp->sumsq_in_workspace == 0 || hp->sumsq_in_workspace == 1, BLOOM_ERR_HPARAM,
                 "sumsq_in_workspace must be 0 or 1");
   BLOOM_REQUIRE(hp->reserved == 0, BLOOM_ERR_HPARAM, "reserved must be 0");
+  BLOOM_REQUIRE(segments != nullptr, BLOOM_ERR_NULL, "segments is NULL");
+  BLOOM_REQUIRE(num_segments >= 1, BLOOM_ERR_SHAPE, "num_segments = %d must be >= 1", num_segments);
+  int64_t end = 0;
+  for (int32_t sgi = 0; sgi < num_segments; ++sgi) {
+    const bloom_adamw_segment& sg = segments[sgi];
+    BLOOM_REQUIRE(sg.offset == end, BLOOM_ERR_SHAPE, "segment %d starts at %lld, expected %lld", sgi,
+                  (long long)sg.offset, (long long)end);
+    BLOOM_REQUIRE(sg.offset % 8 == 0, BLOOM_ERR_ALIGN, "segment %d offset %lld is not a multiple of 8",
+                  sgi, (long long)sg.offset);
+    BLOOM_REQUIRE(sg.length >= 1 || (n == 0 && num_segments == 1), BLOOM_ERR_SHAPE,
+                  "segment %d has length %lld", sgi, (long long)sg.length);
+    BLOOM_REQUIRE(finite_nonneg(sg.weight_decay), BLOOM_ERR_HPARAM,
+                  "segment %d weight_decay must be finite and >= 0", sgi);
+    end += sg.length;
+  }
+  BLOOM_REQUIRE(end == n, BLOOM_ERR_SHAPE, "segments end at %lld, n = %lld", (long long)end, (long long)n);
   if (n == 0) return BLOOM_OK;
   BLOOM_REQUIRE_PTR(master);
   BLOOM_REQUIRE_PTR(exp_avg);
@@ -355,7 +373,6 @@ extern "C" bloom_status bloom_bf16_adamw_step(float* master, float* exp_avg, flo
   k.step_size = (float)(hp->lr / bc1);
   k.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
   k.eps = (float)hp->eps;
-  k.lr_wd = (float)(hp->lr * hp->weight_decay);
 
   char* ws = static_cast<char*>(workspace);
   double* partial = reinterpret_cast<double*>(ws + w.partial_off);
@@ -365,15 +382,51 @@ extern "C" bloom_status bloom_bf16_adamw_step(float* master, float* exp_avg, flo
   if (!hp->sumsq_in_workspace) {
     hipLaunchKernelGGL(sumsq_kernel, dim3((unsigned)parts), dim3(kBlock), 0, stream, grad_acc, n,
                        partial);
-    if (bloom_status st = launch_status("bloom_bf16_adamw_step: norm")) return st;
+    if (bloom_status st = launch_status(name)) return st;
   }
   const int64_t chunk = (parts + kStage2Blocks - 1) / kStage2Blocks;
   hipLaunchKernelGGL(partial_reduce_kernel, dim3(kStage2Blocks), dim3(kBlock), 0, stream, partial,
                      parts, chunk, stage2);
   hipLaunchKernelGGL(norm_finalize_kernel, dim3(1), dim3(kBlock), 0, stream, stage2,
                      hp->max_grad_norm, state, grad_norm_out);
-  if (bloom_status st = launch_status("bloom_bf16_adamw_step: clip")) return st;
-  hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)parts), dim3(kBlock), 0, stream, master, exp_avg,
-                     exp_avg_sq, param_bf16, grad_acc, n, state, k);
-  return launch_status("bloom_bf16_adamw_step: update");
+  if (bloom_status st = launch_status(name)) return st;
+  for (int32_t sgi = 0; sgi < num_segments; ++sgi) {
+    const bloom_adamw_segment& sg = segments[sgi];
+    k.lr_wd = (float)(hp->lr * sg.weight_decay);
+    const int64_t o = sg.offset;
+    hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)quad_blocks(sg.length)), dim3(kBlock), 0, stream,
+                       master + o, exp_avg + o, exp_avg_sq + o, param_bf16 + o, grad_acc + o, sg.length,
+                       state, k);
+    if (bloom_status st = launch_status(name)) return st;
+  }
+  return BLOOM_OK;
+}
+
+}  // namespace
+}  // namespace bloom
+
+extern "C" bloom_status bloom_bf16_adamw_step(float* master, float* exp_avg, float* exp_avg_sq,
+                                              bloom_bf16* param_bf16, const float* grad_acc,
+                                              int64_t n, const bloom_adamw_hparams* hp,
+                                              float* grad_norm_out, void* workspace,
+                                              size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  BLOOM_REQUIRE(hp != nullptr, BLOOM_ERR_NULL, "hp is NULL");
+  BLOOM_REQUIRE(finite_nonneg(hp->weight_decay), BLOOM_ERR_HPARAM,
+                "weight_decay must be finite and >= 0");
+  const bloom_adamw_segment all = {0, n, hp->weight_decay};
+  return adamw_step_impl("bloom_bf16_adamw_step", master, exp_avg, exp_avg_sq, param_bf16, grad_acc, n, hp,
+                         &all, 1, grad_norm_out, workspace, workspace_bytes, stream);
+}
+
+extern "C" bloom_status bloom_bf16_adamw_step_segments(float* master, float* exp_avg, float* exp_avg_sq,
+                                                       bloom_bf16* param_bf16, const float* grad_acc,
+                                                       int64_t n, const bloom_adamw_hparams* hp,
+                                                       const bloom_adamw_segment* segments,
+                                                       int32_t num_segments, float* grad_norm_out,
+                                                       void* workspace, size_t workspace_bytes,
+                                                       hipStream_t stream) {
+  clear_error();
+  return adamw_step_impl("bloom_bf16_adamw_step_segments", master, exp_avg, exp_avg_sq, param_bf16, grad_acc,
+                         n, hp, segments, num_segments, grad_norm_out, workspace, workspace_bytes, stream);
 }

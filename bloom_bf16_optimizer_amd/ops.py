@@ -14,7 +14,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import AdamWHParams, check
+from ._lib import AdamWHParams, AdamWSegment, check
 
 BF16 = torch.bfloat16
 F32 = torch.float32
@@ -215,3 +215,30 @@ def bloom_bf16_adamw_step(master, exp_avg, exp_avg_sq, param_bf16, grad_acc, hp:
         _ptr(param_bf16, BF16, "param_bf16"), _ptr(grad_acc, F32, "grad_acc"), n, ctypes.byref(hp),
         _ptr(grad_norm_out, F32, "grad_norm_out"), _ptr(workspace, workspace.dtype, "workspace"), wsb,
         _stream()))
+
+
+def bloom_bf16_adamw_step_segments(master, exp_avg, exp_avg_sq, param_bf16, grad_acc, hp: AdamWHParams,
+                                   segments, grad_norm_out, workspace) -> None:
+    """segments: sequence of (offset, length, weight_decay) tiling [0, n)."""
+    n = master.numel()
+    for t, name in ((exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"), (param_bf16, "param_bf16"),
+                    (grad_acc, "grad_acc")):
+        if t.numel() != n:
+            raise ValueError(f"{name} must have {n} elements")
+    segs = (AdamWSegment * max(len(segments), 1))(*[AdamWSegment(int(o), int(l), float(w))
+                                                     for o, l, w in segments])
+    wsb = workspace.numel() * workspace.element_size()
+    lib = _lib.load()
+    check("bloom_bf16_adamw_step_segments", lib.bloom_bf16_adamw_step_segments(
+        _ptr(master, F32, "master"), _ptr(exp_avg, F32, "exp_avg"), _ptr(exp_avg_sq, F32, "exp_avg_sq"),
+        _ptr(param_bf16, BF16, "param_bf16"), _ptr(grad_acc, F32, "grad_acc"), n, ctypes.byref(hp), segs,
+        len(segments), _ptr(grad_norm_out, F32, "grad_norm_out"), _ptr(workspace, workspace.dtype, "workspace"),
+        wsb, _stream()))
+
+
+def bloom_lr_warmup_cosine(step: int, max_lr: float, min_lr: float, warmup_steps: int, decay_steps: int) -> float:
+    out = ctypes.c_double()
+    lib = _lib.load()
+    check("bloom_lr_warmup_cosine", lib.bloom_lr_warmup_cosine(step, max_lr, min_lr, warmup_steps, decay_steps,
+                                                               ctypes.byref(out)))
+    return out.value

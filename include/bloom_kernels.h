@@ -257,6 +257,47 @@ bloom_status bloom_bf16_adamw_step(float* master, float* exp_avg, float* exp_avg
                                    const bloom_adamw_hparams* hp, float* grad_norm_out,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* One contiguous range of the flat optimizer buffers with its own weight
+ * decay: the optimizer group splitting of [overview] "工程挑战" (for example,
+ * no decay on biases and LayerNorm weights). */
+typedef struct {
+  int64_t offset;      /* first element; a multiple of 8 */
+  int64_t length;      /* elements, >= 1 */
+  double weight_decay; /* finite, >= 0 */
+} bloom_adamw_segment;
+
+/* bloom_bf16_adamw_step with per-segment weight decay.  The norm and the clip
+ * coefficient are global over all n elements, exactly as in
+ * bloom_bf16_adamw_step; the update of the elements of segment s uses
+ * segments[s].weight_decay in place of hp->weight_decay (which is ignored).
+ * segments: host array of num_segments >= 1 entries in increasing offset
+ * order that tile [0, n) exactly (the first starts at 0, each starts where
+ * the previous ends, the last ends at n).  Other arguments, the workspace
+ * and hp->sumsq_in_workspace are as for bloom_bf16_adamw_step.  One segment
+ * {0, n, wd} gives bit for bit the result of bloom_bf16_adamw_step with
+ * hp->weight_decay = wd.
+ */
+bloom_status bloom_bf16_adamw_step_segments(float* master, float* exp_avg, float* exp_avg_sq,
+                                            bloom_bf16* param_bf16, const float* grad_acc, int64_t n,
+                                            const bloom_adamw_hparams* hp,
+                                            const bloom_adamw_segment* segments,
+                                            int32_t num_segments, float* grad_norm_out,
+                                            void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream);
+
+/* Learning rate for optimizer step `step` (1-based), host only.  [mini] 3
+ * (lr 6e-5, min_lr 1e-6, cosine decay, 500 warmup iterations, 100000
+ * iterations):
+ *   step <= warmup_steps:  max_lr * step / warmup_steps
+ *   step >= decay_steps:   min_lr
+ *   otherwise:             min_lr + (max_lr - min_lr) * (1 + cos(pi * q)) / 2,
+ *                          q = (step - warmup_steps) / (decay_steps - warmup_steps)
+ * Requires step >= 1, 0 <= min_lr <= max_lr (finite) and
+ * 0 <= warmup_steps < decay_steps; writes *lr_out (FP64).
+ */
+bloom_status bloom_lr_warmup_cosine(int64_t step, double max_lr, double min_lr, int64_t warmup_steps,
+                                    int64_t decay_steps, double* lr_out);
+
 #ifdef __cplusplus
 }
 #endif

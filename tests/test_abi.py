@@ -37,7 +37,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for required in ["bloom_layernorm_fwd", "bloom_layernorm_bwd", "bloom_layernorm_residual_fwd",
+    for required in ["bloom_bf16_adamw_step_segments", "bloom_lr_warmup_cosine",
+                     "bloom_layernorm_fwd", "bloom_layernorm_bwd", "bloom_layernorm_residual_fwd",
                      "bloom_layernorm_residual_bwd", "bloom_alibi_softmax_fwd",
                      "bloom_alibi_softmax_bwd", "bloom_bias_gelu_fwd", "bloom_bias_gelu_bwd",
                      "bloom_bf16_grad_accumulate", "bloom_bf16_adamw_step", "bloom_alibi_slopes"]:
@@ -51,7 +52,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.bloom_abi_version() == 3
+    assert lib.bloom_abi_version() == 4
     assert lib.bloom_status_string(0) == b"ok"
     assert lib.bloom_status_string(4) == b"workspace too small"
     assert lib.bloom_status_string(99) == b"unknown status"
@@ -169,3 +170,38 @@ def test_optimizer_validation(lib):
     assert acc(p, p, -1, 1, None) == SHAPE
     assert acc(p, None, 10, 1, None) == NULL
     assert acc(p, p, 0, 0, None) == OK
+
+
+def test_adamw_segments_validation(lib):
+    p = FAKE
+    hp = _lib.AdamWHParams(6e-5, 0.9, 0.999, 1e-8, 0.01, 1.0, 1, 0, 0)
+    ws = lib.bloom_bf16_adamw_workspace_size(1000)
+    seg = _lib.AdamWSegment
+    step = lib.bloom_bf16_adamw_step_segments
+
+    def call(segs, n=1000):
+        arr = (seg * len(segs))(*[seg(*s) for s in segs])
+        return step(p, p, p, p, p, n, ctypes.byref(hp), arr, len(segs), None, p, ws, None)
+
+    assert call([(0, 600, 0.01), (608, 392, 0.0)]) == SHAPE        # gap
+    assert call([(0, 604, 0.01), (604, 396, 0.0)]) == ALIGN        # second offset not a multiple of 8
+    assert call([(0, 600, 0.01), (600, 300, 0.0)]) == SHAPE        # does not reach n
+    assert call([(0, 1000, -1.0)]) == HPARAM
+    assert call([(0, 1000, float("inf"))]) == HPARAM
+    assert step(p, p, p, p, p, 1000, ctypes.byref(hp), None, 1, None, p, ws, None) == NULL
+    assert call([(0, 0, 0.01)], n=0) == OK
+
+
+def test_lr_schedule_host_function_matches_oracle(lib):
+    from oracle.optimizer import lr_warmup_cosine
+    out = ctypes.c_double()
+    for t in [1, 2, 250, 499, 500, 501, 1000, 24875, 50250, 99999, 100000, 123456]:
+        assert lib.bloom_lr_warmup_cosine(t, 6e-5, 1e-6, 500, 100000, ctypes.byref(out)) == OK
+        want = lr_warmup_cosine(t, 6e-5, 1e-6, 500, 100000)
+        assert abs(out.value - want) <= 1e-15 * want, t
+    assert lib.bloom_lr_warmup_cosine(7, 1.0, 0.0, 0, 10, ctypes.byref(out)) == OK
+    assert abs(out.value - lr_warmup_cosine(7, 1.0, 0.0, 0, 10)) < 1e-16
+    assert lib.bloom_lr_warmup_cosine(0, 6e-5, 1e-6, 500, 100000, ctypes.byref(out)) == HPARAM
+    assert lib.bloom_lr_warmup_cosine(5, 1e-6, 6e-5, 500, 100000, ctypes.byref(out)) == HPARAM
+    assert lib.bloom_lr_warmup_cosine(5, 6e-5, 1e-6, 500, 500, ctypes.byref(out)) == HPARAM
+    assert lib.bloom_lr_warmup_cosine(5, 6e-5, 1e-6, 500, 1000, None) == NULL

@@ -280,3 +280,45 @@ def test_shard_optimizer_full_size():
     (rp, rm, rv, rpb), f64, terms, _ = _oracle_step(p, z, z, ref_acc, 1, norm=rnorm)
     _compare_step("shard", tp[ti].cpu().numpy(), tm[ti].cpu().numpy(), tv[ti].cpu().numpy(),
                   host_bf16(param[ti]), f64, terms, rpb)
+
+
+@pytest.mark.parametrize("n,segs,fused", [
+    (1_000_003, [(0, 600_000, 0.01), (600_000, 300_000, 0.0), (900_000, 100_003, 0.05)], False),
+    (1_000_003, [(0, 999_992, 0.01), (999_992, 11, 0.0)], True),
+    (24, [(0, 8, 0.0), (8, 8, 0.1), (16, 8, 0.01)], False)])
+def test_weight_decay_segments(n, segs, fused):
+    """Per-segment weight decay with one global norm and clip, against the
+    oracle; one segment spanning everything reproduces the flat step's bits."""
+    require_gpu()
+    seed, step, mb = 5, 3, 2
+    tp, p = gen((n,), seed, W.S_OPT_PARAM, W.PARAM_SIGMA, dtype=torch.float32)
+    tm, m = gen((n,), seed, W.S_OPT_M, W.M_SIGMA, dtype=torch.float32)
+    tv, v = gen((n,), seed, W.S_OPT_V, W.V_SIGMA, dtype=torch.float32, absolute=True)
+    ws = _workspace(n)
+    acc_t = _accumulate_gpu(n, seed, mb, ws=ws if fused else None)
+    acc = acc_t.cpu().numpy()
+    ref_acc = _accumulate_oracle(np.arange(n, dtype=np.uint64), seed, mb)
+    assert np.array_equal(acc.view(np.uint32), ref_acc.view(np.uint32))
+    # the flat step with one full segment, on copies, for the bit-identity check
+    cp, cm, cv = tp.clone(), tm.clone(), tv.clone()
+    param = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    norm = torch.empty(1, dtype=torch.float32, device="cuda")
+    ops.bloom_bf16_adamw_step_segments(tp, tm, tv, param, acc_t, _hp(step, fused), segs, norm, ws)
+    torch.cuda.synchronize()
+    rp, rm, rv, rpb, rnorm, c = oopt.bf16_optimizer_step_segments(p, m, v, ref_acc, segs, W.LR, W.BETA1, W.BETA2,
+                                                                 W.ADAM_EPS, W.MAX_GRAD_NORM, step)
+    assert abs(norm.item() - rnorm) <= 1e-6 * rnorm
+    gm, gmm, gv, gpb = tp.cpu().numpy(), tm.cpu().numpy(), tv.cpu().numpy(), host_bf16(param)
+    for off, length, wd in segs:
+        sl = slice(off, off + length)
+        _, f64, terms = oopt.adamw_update(p[sl], m[sl], v[sl], ref_acc[sl], c, W.LR, W.BETA1, W.BETA2, W.ADAM_EPS,
+                                          wd, step, return_f64=True)
+        _compare_step(f"segment {off}+{length} wd={wd}", gm[sl], gmm[sl], gv[sl], gpb[sl], f64, terms, rpb[sl])
+    if not fused:
+        # one segment over everything == the flat entry point with that weight decay, bit for bit
+        fp, fm, fv = cp.clone(), cm.clone(), cv.clone()
+        p2, p3 = torch.empty_like(param), torch.empty_like(param)
+        ops.bloom_bf16_adamw_step_segments(cp, cm, cv, p2, acc_t, _hp(step), [(0, n, segs[0][2])], norm, ws)
+        ops.bloom_bf16_adamw_step(fp, fm, fv, p3, acc_t, _hp(step, weight_decay=segs[0][2]), norm, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(cp, fp) and torch.equal(cm, fm) and torch.equal(cv, fv) and torch.equal(p2, p3)
