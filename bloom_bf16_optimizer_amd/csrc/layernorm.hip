@@ -340,7 +340,7 @@ __device__ __forceinline__ uint32_t lds_offset(const lds_uint4* p) { return (uin
 
 // One 16-byte-per-lane transfer from global memory into LDS at m0 + lane*16.
 __device__ __forceinline__ void dma16(const uint4* src, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                :
                : "v"(src), "s"(m0)
                : "memory", "m0");
