@@ -40,6 +40,7 @@ if ROOT not in sys.path:
 
 METRIC = "achieved HBM GB/s (% of peak) per fused kernel; AdamW step ms @3.67B shard"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 GRAD_BUFFERS = 8
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
@@ -62,6 +63,10 @@ def bytes_model(sh, n, mb):
         # fused LayerNorm + residual: reads x, r and writes h, y / reads dy, dres, h and writes dh
         "layernorm_residual_fwd": rows * hid * 8 + hid * 4 + rows * 8,
         "layernorm_residual_bwd": rows * hid * 8 + hid * 2 + rows * 8 + hid * 4,
+        # fused ALiBi attention forward: q, k, v read, o written (bf16), lse written (fp32)
+        "alibi_attention_fwd": b * h * s * sh["head_dim"] * 2 * 4 + b * h * s * 4,
+        # ... and its MFMA work: q.k and p.v take 2*D flops each per causal (query, key <= query) pair
+        "_attention_flops": 2 * 2 * b * h * (s * (s + 1) // 2) * sh["head_dim"],
         "alibi_softmax_fwd": live * 2 + full * 2,
         "alibi_softmax_bwd": live * 4 + full * 2,
         "bias_gelu_fwd": grows * gcols * 4 + gcols * 2,
@@ -211,7 +216,19 @@ def run_gpu(args):
     step_fused = [(name, make(0)) for name, make, _ in fused]
     # Kernels measured in the sweep only (not rows of the step): LayerNorm fused
     # with the residual connection, at the same [2048, 14336] shape.
-    sweep_only = [("layernorm_residual_fwd", lnr_fwd_set, 4), ("layernorm_residual_bwd", lnr_bwd_set, 4)]
+    hd = X.softmax.head_dim
+
+    def att_fwd_set(s):
+        q = fill((smb, smh, sms, hd), W.S_ATT_Q, 1.0, s=s)
+        k = fill((smb, smh, sms, hd), W.S_ATT_K, 1.0, s=s)
+        v = fill((smb, smh, sms, hd), W.S_ATT_V, 1.0, s=s)
+        o = torch.empty_like(q)
+        lse = torch.empty((smb, smh, sms), dtype=f32, device=dev)
+        return lambda: ops.bloom_alibi_attention_fwd(q, k, v, o, lse, X.softmax.head_offset, X.softmax.total_heads,
+                                                     scale)
+
+    sweep_only = [("layernorm_residual_fwd", lnr_fwd_set, 4), ("layernorm_residual_bwd", lnr_bwd_set, 4),
+                  ("alibi_attention_fwd", att_fwd_set, 4)]
 
     log(f"bench: allocating the shard workload (n = {n:,}, {GRAD_BUFFERS} gradient buffers)")
     master = fill((n,), W.S_OPT_PARAM, W.PARAM_SIGMA, dtype=f32)
@@ -297,7 +314,7 @@ def run_gpu(args):
         b.synchronize()
         sweep[name] = a.elapsed_time(b) / reps
         del fns
-    shapes = {"ln": (rows, hid), "sm": (smb, smh, sms), "gelu": (grows, gcols)}
+    shapes = {"ln": (rows, hid), "sm": (smb, smh, sms), "gelu": (grows, gcols), "head_dim": hd}
     return ms_step, in_step, sweep, bytes_model(shapes, n, mb), n, mb
 
 
@@ -404,6 +421,13 @@ def main():
                       else "events around each launch in the timed steps"}
         if k in sweep:
             kernels[k]["in_step_ms"] = round(in_step[k], 4) if k in in_step else None
+    if "alibi_attention_fwd" in kernels:
+        # causal: q.k and p.v each take 2*D flops for every (query, key <= query) pair
+        flops = bts["_attention_flops"]
+        tf = flops / (per["alibi_attention_fwd"] * 1e-3) / 1e12
+        kernels["alibi_attention_fwd"].update({"flops": flops, "TFLOP/s": round(tf, 1),
+                                               "frac_of_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                                               "bound": "mfma (bf16 dense, 2500 TFLOP/s)"})
     dom = "grad_accumulate"
     dom_gbs = bts[dom] / (per[dom] * 1e-3) / 1e9
     traffic = measured_traffic(dom)

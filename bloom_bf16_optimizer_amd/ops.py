@@ -145,6 +145,20 @@ def bloom_alibi_softmax_bwd(probs, dprobs, dscores, scale: float) -> None:
         b, h, s, scale, _stream()))
 
 
+def bloom_alibi_attention_fwd(q, k, v, o, lse, head_offset: int, total_heads: int, scale: float) -> None:
+    if q.dim() != 4:
+        raise ValueError("q must be [batch, heads, seq, head_dim]")
+    b, h, s, d = q.shape
+    for t, name in ((k, "k"), (v, "v"), (o, "o")):
+        _same(q, t, f"q/{name}")
+    if lse.numel() != b * h * s:
+        raise ValueError("lse must have batch*heads*seq elements")
+    lib = _lib.load()
+    check("bloom_alibi_attention_fwd", lib.bloom_alibi_attention_fwd(
+        _ptr(q, BF16, "q"), _ptr(k, BF16, "k"), _ptr(v, BF16, "v"), _ptr(o, BF16, "o"), _ptr(lse, F32, "lse"),
+        b, h, s, d, head_offset, total_heads, scale, _stream()))
+
+
 def bloom_bias_gelu_fwd(x, bias, y) -> None:
     rows, cols = _rows_cols(x)
     _same(x, y, "x/y")

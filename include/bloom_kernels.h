@@ -171,6 +171,25 @@ bloom_status bloom_alibi_softmax_bwd(const bloom_bf16* probs, const bloom_bf16* 
                                      bloom_bf16* dscores, int64_t batch, int32_t heads,
                                      int64_t seq, float scale, hipStream_t stream);
 
+/* Fused causal attention with the ALiBi bias, forward, flash-style: the
+ * L x L scores are never written.  [overview] "架构微调" (ALiBi in place of
+ * position embeddings) and "融合 CUDA 核" (the fused scale + mask + softmax,
+ * here applied between Q K^T and V); [3d] 4.3 (trained at 2048 tokens,
+ * extrapolated to 8192).
+ *   z_ij  = scale*(q_i . k_j) - slope_h*(i - j) for keys j <= i; j > i masked
+ *   o_i   = sum_j softmax_j(z_i) v_j   (P rounded to bf16 for the product,
+ *           FP32 accumulation)
+ *   lse_i = ln sum_{j<=i} exp(z_ij)     (FP32; what a backward needs)
+ * q, k, v, o [batch, heads, seq, head_dim] bf16 row-major; lse [batch, heads,
+ * seq] fp32.  head_dim 32, 64 or 128; seq a multiple of 8, <=
+ * BLOOM_MAX_SEQ; slopes as for bloom_alibi_softmax_fwd (heads [head_offset,
+ * head_offset+heads) of a total_heads model).  o must not overlap q, k, v.
+ */
+bloom_status bloom_alibi_attention_fwd(const bloom_bf16* q, const bloom_bf16* k, const bloom_bf16* v,
+                                       bloom_bf16* o, float* lse, int64_t batch, int32_t heads,
+                                       int64_t seq, int32_t head_dim, int32_t head_offset,
+                                       int32_t total_heads, float scale, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * bias + GeLU forward.  [overview] "融合 CUDA 核" (bias + GeLU fusion); the
  * MLP's GeLU(XA) of [3d] 2.1.  tanh form (Hendrycks and Gimpel,

@@ -37,7 +37,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for required in ["bloom_bf16_adamw_step_segments", "bloom_lr_warmup_cosine",
+    for required in ["bloom_alibi_attention_fwd", "bloom_bf16_adamw_step_segments", "bloom_lr_warmup_cosine",
                      "bloom_layernorm_fwd", "bloom_layernorm_bwd", "bloom_layernorm_residual_fwd",
                      "bloom_layernorm_residual_bwd", "bloom_alibi_softmax_fwd",
                      "bloom_alibi_softmax_bwd", "bloom_bias_gelu_fwd", "bloom_bias_gelu_bwd",
@@ -52,7 +52,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.bloom_abi_version() == 4
+    assert lib.bloom_abi_version() == 5
     assert lib.bloom_status_string(0) == b"ok"
     assert lib.bloom_status_string(4) == b"workspace too small"
     assert lib.bloom_status_string(99) == b"unknown status"
@@ -205,3 +205,15 @@ def test_lr_schedule_host_function_matches_oracle(lib):
     assert lib.bloom_lr_warmup_cosine(5, 1e-6, 6e-5, 500, 100000, ctypes.byref(out)) == HPARAM
     assert lib.bloom_lr_warmup_cosine(5, 6e-5, 1e-6, 500, 500, ctypes.byref(out)) == HPARAM
     assert lib.bloom_lr_warmup_cosine(5, 6e-5, 1e-6, 500, 1000, None) == NULL
+
+
+def test_attention_validation(lib):
+    p = FAKE
+    f = lib.bloom_alibi_attention_fwd
+    assert f(p, p, p, p, p, 1, 4, 100, 128, 0, 4, 0.1, None) == SHAPE       # seq not a multiple of 8
+    assert f(p, p, p, p, p, 1, 4, 64, 96, 0, 4, 0.1, None) == SHAPE        # head_dim not 32/64/128
+    assert f(p, p, p, p, p, 1, 4, 64, 128, 2, 4, 0.1, None) == SHAPE       # heads outside the model
+    assert f(p, p, p, p, p, 1, 4, 64, 128, 0, 4, float("nan"), None) == HPARAM
+    assert f(p, p, p, None, p, 1, 4, 64, 128, 0, 4, 0.1, None) == NULL
+    assert f(p, p, p, p + 8, p, 1, 4, 64, 128, 0, 4, 0.1, None) == ALIGN
+    assert f(p, p, p, p, p, 0, 4, 64, 128, 0, 4, 0.1, None) == OK           # empty

@@ -1,0 +1,88 @@
+"""GPU parity: fused causal attention with the ALiBi bias (forward), against the oracle.
+
+Tolerance: P is rounded to bf16 before the P V product (relative 2^-9 per
+weight), the products accumulate in FP32 and the exponentials use the
+hardware exp2, so an output element may differ from the exact value by about
+2^-8 * sum_j p_j |v_j| (the oracle's condition magnitude) beyond one bf16
+spacing; the check passes that magnitude scaled to that bound.  lse is FP32:
+within 1e-5 * (1 + |lse|).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from synth import workloads as W
+from oracle import attention as oat
+from parity_helpers import TERM_REL, check_bf16, dev_bf16, gen, host_bf16, require_gpu, sample_rows
+from bloom_bf16_optimizer_amd import ops
+
+pytestmark = pytest.mark.gpu
+
+P_REL = 2.0 ** -8  # bound on the relative effect of the bf16 rounding of P
+
+
+def _inputs(seed, b, h, s, d):
+    return tuple(gen((b, h, s, d), seed, st, 1.0)[1] for st in (W.S_ATT_Q, W.S_ATT_K, W.S_ATT_V))
+
+
+def _run(q, k, v, head_offset, total_heads, scale):
+    b, h, s, d = q.shape
+    tq, tk, tv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    to = torch.empty_like(tq)
+    tl = torch.empty((b, h, s), dtype=torch.float32, device="cuda")
+    ops.bloom_alibi_attention_fwd(tq, tk, tv, to, tl, head_offset, total_heads, scale)
+    torch.cuda.synchronize()
+    return host_bf16(to), tl.cpu().numpy()
+
+
+def _check(tag, q, k, v, head_offset, total_heads, scale, rows=None):
+    o, lse = _run(q, k, v, head_offset, total_heads, scale)
+    (ro, rl), (of, lf, terms) = oat.attention_fwd(q, k, v, total_heads, head_offset, scale, rows=rows,
+                                                   return_f64=True)
+    if rows is not None:
+        o, lse = o[:, :, rows], lse[:, :, rows]
+    check_bf16(f"{tag} o", o, ro, exact=of, terms=terms * (P_REL / TERM_REL))
+    err = np.abs(lse.astype(np.float64) - lf)
+    assert np.all(err <= 1e-5 * (1 + np.abs(lf))), f"{tag} lse: max err {err.max()}"
+
+
+@pytest.mark.parametrize("wl", [W.TINY, W.MINI, W.SHARD], ids=lambda w: w.name)
+def test_attention_workloads(wl):
+    require_gpu()
+    s = wl.softmax
+    q, k, v = _inputs(wl.seed, s.batch, s.heads, s.seq, s.head_dim)
+    rows = None if s.seq <= 256 else sample_rows(s.seq, 96, wl.seed, must=(0, 1, 63, 64, 127, 128, s.seq - 1))
+    _check(wl.name, q, k, v, s.head_offset, s.total_heads, s.scale, rows)
+
+
+@pytest.mark.timeout(900)
+def test_attention_long_context_sampled():
+    require_gpu()
+    wl = W.LONG
+    s = wl.softmax
+    q, k, v = _inputs(wl.seed, s.batch, 4, s.seq, s.head_dim)   # 4 of the 28 heads: heads 0..3 of 112
+    rows = sample_rows(s.seq, 24, wl.seed, must=(0, 2047, 2048, s.seq - 1))
+    _check("long 8192", q, k, v, s.head_offset, s.total_heads, s.scale, rows)
+
+
+# seq not a multiple of the 128-query or 64-key blocks; head_offset inside a
+# larger model; every head dimension.
+@pytest.mark.parametrize("b,h,s,d,off,tot", [(1, 1, 8, 32, 0, 1), (2, 3, 24, 64, 5, 12), (1, 2, 136, 128, 0, 112),
+                                            (1, 2, 200, 64, 100, 112), (3, 1, 72, 32, 3, 6), (1, 1, 264, 128, 0, 16)])
+def test_attention_ragged(b, h, s, d, off, tot):
+    require_gpu()
+    q, k, v = _inputs(41, b, h, s, d)
+    _check(f"ragged {b}x{h}x{s}x{d}", q, k, v, off, tot, 1.0 / d ** 0.5)
+
+
+def test_attention_constant_values_and_determinism():
+    require_gpu()
+    q, k, v = _inputs(42, 1, 2, 192, 64)
+    v[:] = v[0, 0, 0]                          # every value row equal: o = that row exactly (weights sum to 1)
+    o, _ = _run(q, k, v, 0, 2, 0.125)
+    assert np.array_equal(o, np.broadcast_to(v[0, 0, 0], o.shape)) or \
+        np.all(np.abs(oat.to_f64(o) - oat.to_f64(v)) <= 2 ** -8 * np.abs(oat.to_f64(v)))
+    o2, l2 = _run(q, k, v, 0, 2, 0.125)
+    o3, l3 = _run(q, k, v, 0, 2, 0.125)
+    assert np.array_equal(o2, o3) and np.array_equal(l2, l3)
