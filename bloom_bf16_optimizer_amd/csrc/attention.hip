@@ -110,6 +110,112 @@ __device__ __forceinline__ void attn_store(const AttnStage<D>& st, uint16_t* ks,
   }
 }
 
+// A lane's running state: its share (keys of its lane half) of the output
+// accumulators and of the softmax denominator, and the row's running max.
+template <int D>
+struct AttnState {
+  f32x16_t oacc[D / 32];
+  float m;  // running max of the row's logits, base 2, shared by lanes l and l^32
+  float l;  // sum of this lane's weights (FP32, unrounded), scaled to m
+};
+
+// Headroom, in base-2 units, the running max may lag the true max by: the
+// output is rescaled only when a block raises the row max by more than this,
+// so weights stay below 2^8 and the accumulators in FP32 range.
+constexpr float kAttnLazyMax = 8.0f;
+
+// One key block for one wave.  The scores come out of the MFMAs as
+//   S = q.k + (key - k0) * slope/scale
+// (the ALiBi offset inside the block enters as one more MFMA k-step, from the
+// constant fragments kx and qx), so the base-2 logit is
+//   t = S*scale2 + slope2*(k0 - q),
+// the second term being one number per lane per block.  DIAG: some key of
+// the block is after some query of the wave, so the causal mask applies.
+template <int D, bool DIAG>
+__device__ __forceinline__ void attn_block(AttnState<D>& st, const uint16_t* __restrict__ ksb,
+                                           const uint16_t* __restrict__ vtb, const bf16x8_t (&qf)[D / 16],
+                                           const bf16x8_t (&kx)[2], const bf16x8_t& qx, float scale2,
+                                           float slope2, int k0, int qi, int half, int col) {
+  constexpr int KS = D / 16, DT = D / 32, KROW = D + 8, VROW = kAttnBlockN + 8;
+  // S^T tiles: keys k0 + 32*kt + (8*(i/4) + 4*half + i%4), query col.  The two
+  // tiles' accumulation chains alternate, and the K fragments of step kk+1
+  // are read while step kk's products run.
+  const f32x16_t zero = {};
+  f32x16_t s[2];
+  s[0] = mfma32(kx[0], qx, zero);
+  s[1] = mfma32(kx[1], qx, zero);
+  const uint16_t* krow0 = &ksb[col * KROW + 8 * half];
+  const uint16_t* krow1 = krow0 + 32 * KROW;
+  uint4 a0 = *reinterpret_cast<const uint4*>(krow0);
+  uint4 a1 = *reinterpret_cast<const uint4*>(krow1);
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    uint4 n0 = a0, n1 = a1;
+    if (kk + 1 < KS) {
+      n0 = *reinterpret_cast<const uint4*>(krow0 + 16 * (kk + 1));
+      n1 = *reinterpret_cast<const uint4*>(krow1 + 16 * (kk + 1));
+    }
+    s[0] = mfma32(as_bf16x8(a0), qf[kk], s[0]);
+    s[1] = mfma32(as_bf16x8(a1), qf[kk], s[1]);
+    a0 = n0;
+    a1 = n1;
+  }
+  if (DIAG) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (k0 + 32 * kt + 8 * (i / 4) + 4 * half + (i % 4) > qi) s[kt][i] = -INFINITY;
+  }
+  // Row max: scale2 > 0, so the max of S*scale2 is scale2 times the max of S.
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+  const float shift = slope2 * (float)(k0 - qi);
+  float bm = fmaf(mx, scale2, shift);
+  bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+  if (__ballot(bm > st.m + kAttnLazyMax) != 0) {  // wave-uniform: rescale to a new max
+    const float m_new = fmaxf(st.m, bm);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);  // 0 on the first block
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.oacc[dt][i] *= alpha;
+    st.l *= alpha;
+    st.m = m_new;
+  }
+  const float c = fmaf(slope2, (float)(k0 - qi), -st.m);
+  bf16x8_t pf[4];
+  float l = st.l;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], scale2, c));
+      l += p;
+      pf[2 * kt + i / 8][i % 8] = (__bf16)p;
+    }
+  st.l = l;
+  // O^T += V^T P^T over the 4 key steps of the block; the k order of step st
+  // is keys 16*st + 4*half + {0..3, 8..11} for lane half `half` (key step
+  // outer, head-dim tile inner: the DT accumulation chains alternate).
+#pragma unroll
+  for (int stp = 0; stp < 4; ++stp) {
+    uint4 vf[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint16_t* row = &vtb[(dt * 32 + col) * VROW + 16 * stp + 4 * half];
+      const uint2 lo = *reinterpret_cast<const uint2*>(row);
+      const uint2 hi = *reinterpret_cast<const uint2*>(row + 8);
+      vf[dt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) st.oacc[dt] = mfma32(as_bf16x8(vf[dt]), pf[stp], st.oacc[dt]);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void attention_fwd_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
@@ -137,6 +243,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_fwd_kernel(
   const int q0 = qb * kAttnBlockM + w * 32;  // this wave's first query
   const int qi = q0 + col;                   // this lane's query
   const bool qvalid = qi < seq;
+  const bool wave_live = q0 < seq;
 
   // Q^T operand fragments: lane supplies q[qi][16*kk + 8*half .. +8].
   bf16x8_t qf[KS];
@@ -145,95 +252,61 @@ __global__ __launch_bounds__(kAttnThreads) void attention_fwd_kernel(
     const uint4 u = qvalid ? q[(base + qi) * VPR + 2 * kk + half] : make_uint4(0u, 0u, 0u, 0u);
     qf[kk] = as_bf16x8(u);
   }
+  // ALiBi offset fragments: k-slots 0..2 of the lower lane half carry the key
+  // offset in the block (an integer < 64, exact in bf16) against slope/scale
+  // split into three bf16 parts; every other slot is zero.
+  bf16x8_t kx[2], qx;
+  {
+    const float cs = slope2 / scale2;  // slope/scale
+    const __bf16 c1 = (__bf16)cs;
+    const float r1 = cs - (float)c1;
+    const __bf16 c2 = (__bf16)r1;
+    const __bf16 c3 = (__bf16)(r1 - (float)c2);
+    const __bf16 z = (__bf16)0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool on = half == 0 && j < 3;
+      qx[j] = on ? (j == 0 ? c1 : (j == 1 ? c2 : c3)) : z;
+      kx[0][j] = on ? (__bf16)(float)col : z;
+      kx[1][j] = on ? (__bf16)(float)(col + 32) : z;
+    }
+  }
 
-  f32x16_t oacc[DT];
+  AttnState<D> st;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int i = 0; i < 16; ++i) st.oacc[dt][i] = 0.f;
+  st.m = -INFINITY;
+  st.l = 0.f;
 
+  // Key blocks run from the diagonal back to key 0: the block holding a
+  // row's own key comes first, and with the ALiBi bias falling off with
+  // distance the running max then rarely moves.
   const int wg_last_q = min(seq, (qb + 1) * kAttnBlockM) - 1;
   const int nkb = wg_last_q / kAttnBlockN + 1;
   AttnStage<D> stage;
-  attn_load<D>(stage, k, v, base, 0, seq, t);
+  attn_load<D>(stage, k, v, base, (nkb - 1) * kAttnBlockN, seq, t);
   attn_store<D>(stage, ks[0], vt[0], t);
   __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
+  for (int kb = nkb - 1, buf = 0; kb >= 0; --kb, buf ^= 1) {
     const int k0 = kb * kAttnBlockN;
-    const int buf = kb & 1;
     // next block's loads are in flight during this block's products
-    if (kb + 1 < nkb) attn_load<D>(stage, k, v, base, k0 + kAttnBlockN, seq, t);
-
-    if (k0 <= q0 + 31) {  // else every key of the block is after every query of this wave
-      // S^T tiles: keys 32*kt + (8*(i/4) + 4*half + i%4), query col
-      f32x16_t s[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          const uint4 a = *reinterpret_cast<const uint4*>(&ks[buf][(kt * 32 + col) * KROW + 16 * kk + 8 * half]);
-          s[kt] = mfma32(as_bf16x8(a), qf[kk], s[kt]);
-        }
-      }
-      // z = scale*s + slope*(j - qi), base 2; with j = k0 + 4*half + C_i and
-      // C_i = 32*kt + 8*(i/4) + i%4 a constant, the bias is one fma per score.
-      const float b0 = slope2 * (float)(k0 + 4 * half - qi);
-      const bool diag = k0 + kAttnBlockN - 1 > q0;  // some key of the block is after some query
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ci = 32 * kt + 8 * (i / 4) + (i % 4);
-          float z = fmaf(s[kt][i], scale2, fmaf(slope2, (float)ci, b0));
-          if (diag && k0 + 4 * half + ci > qi) z = -INFINITY;
-          s[kt][i] = z;
-          mx = fmaxf(mx, z);
-        }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // a query past the end: all masked
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-      float psum = 0.f;
-      bf16x8_t pf[4];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(s[kt][i] - m_use);
-          psum += p;
-          pf[2 * kt + i / 8][i % 8] = (__bf16)p;
-        }
-      }
-      l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-      // O^T += V^T P^T over the 4 key steps of the block; the k order of step
-      // st is keys 16*st + 4*half + {0..3, 8..11} for lane half `half`.
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const uint16_t* row = &vt[buf][(dt * 32 + col) * VROW + 16 * st + 4 * half];
-          const uint2 lo = *reinterpret_cast<const uint2*>(row);
-          const uint2 hi = *reinterpret_cast<const uint2*>(row + 8);
-          oacc[dt] = mfma32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pf[st], oacc[dt]);
-        }
-      }
+    if (kb > 0) attn_load<D>(stage, k, v, base, k0 - kAttnBlockN, seq, t);
+    // Every processed block has k0 <= q0 (both are multiples of 32), so each
+    // row has its key k0 unmasked and the first block sets a finite max.
+    if (wave_live && k0 <= q0 + 31) {
+      if (k0 + kAttnBlockN - 1 > q0)
+        attn_block<D, true>(st, ks[buf], vt[buf], qf, kx, qx, scale2, slope2, k0, qi, half, col);
+      else
+        attn_block<D, false>(st, ks[buf], vt[buf], qf, kx, qx, scale2, slope2, k0, qi, half, col);
     }
-    if (kb + 1 < nkb) attn_store<D>(stage, ks[buf ^ 1], vt[buf ^ 1], t);
+    if (kb > 0) attn_store<D>(stage, ks[buf ^ 1], vt[buf ^ 1], t);
     __syncthreads();
   }
 
   // Normalise: the two lane halves hold the sums over complementary keys.
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  const float l_tot = st.l + __shfl_xor(st.l, 32, kWave);
   const float inv = 1.0f / l_tot;
   if (qvalid) {
 #pragma unroll
@@ -241,15 +314,12 @@ __global__ __launch_bounds__(kAttnThreads) void attention_fwd_kernel(
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         // d = 32*dt + 8*g + 4*half + 0..3
-        const uint32_t lo = pack2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv);
-        const uint32_t hi = pack2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
+        const uint32_t lo = pack2(st.oacc[dt][4 * g] * inv, st.oacc[dt][4 * g + 1] * inv);
+        const uint32_t hi = pack2(st.oacc[dt][4 * g + 2] * inv, st.oacc[dt][4 * g + 3] * inv);
         o[(base + qi) * (D / 4) + (32 * dt + 8 * g + 4 * half) / 4] = make_uint2(lo, hi);
       }
     }
-    if (half == 0) {
-      const float m_fin = (m_run == -INFINITY) ? 0.f : m_run;
-      lse[base + qi] = (m_fin + __log2f(l_tot)) * 0.69314718055994530942f;
-    }
+    if (half == 0) lse[base + qi] = (st.m + __log2f(l_tot)) * 0.69314718055994530942f;
   }
 }
 
@@ -277,7 +347,8 @@ extern "C" bloom_status bloom_alibi_attention_fwd(const bloom_bf16* q, const blo
                                                   int32_t total_heads, float scale, hipStream_t stream) {
   clear_error();
   if (bloom_status st = check_attention(batch, heads, seq, head_dim)) return st;
-  BLOOM_REQUIRE(std::isfinite(scale), BLOOM_ERR_HPARAM, "scale must be finite");
+  BLOOM_REQUIRE(std::isfinite(scale) && scale >= 1e-30f, BLOOM_ERR_HPARAM, "scale = %g must be finite and >= 1e-30",
+                (double)scale);
   BLOOM_REQUIRE(total_heads > 0 && head_offset >= 0 && (int64_t)head_offset + heads <= total_heads,
                 BLOOM_ERR_SHAPE, "heads [%d, %d) outside a %d-head model", head_offset, head_offset + heads,
                 total_heads);

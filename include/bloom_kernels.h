@@ -183,7 +183,9 @@ bloom_status bloom_alibi_softmax_bwd(const bloom_bf16* probs, const bloom_bf16* 
  * q, k, v, o [batch, heads, seq, head_dim] bf16 row-major; lse [batch, heads,
  * seq] fp32.  head_dim 32, 64 or 128; seq a multiple of 8, <=
  * BLOOM_MAX_SEQ; slopes as for bloom_alibi_softmax_fwd (heads [head_offset,
- * head_offset+heads) of a total_heads model).  o must not overlap q, k, v.
+ * head_offset+heads) of a total_heads model).  scale > 0 (at least 1e-30;
+ * 1/sqrt(head_dim) in BLOOM), else BLOOM_ERR_HPARAM.  o must not overlap
+ * q, k, v.
  */
 bloom_status bloom_alibi_attention_fwd(const bloom_bf16* q, const bloom_bf16* k, const bloom_bf16* v,
                                        bloom_bf16* o, float* lse, int64_t batch, int32_t heads,

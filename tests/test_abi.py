@@ -214,6 +214,8 @@ def test_attention_validation(lib):
     assert f(p, p, p, p, p, 1, 4, 64, 96, 0, 4, 0.1, None) == SHAPE        # head_dim not 32/64/128
     assert f(p, p, p, p, p, 1, 4, 64, 128, 2, 4, 0.1, None) == SHAPE       # heads outside the model
     assert f(p, p, p, p, p, 1, 4, 64, 128, 0, 4, float("nan"), None) == HPARAM
+    assert f(p, p, p, p, p, 1, 4, 64, 128, 0, 4, -0.1, None) == HPARAM    # the scale must be positive
+    assert f(p, p, p, p, p, 1, 4, 64, 128, 0, 4, 0.0, None) == HPARAM
     assert f(p, p, p, None, p, 1, 4, 64, 128, 0, 4, 0.1, None) == NULL
     assert f(p, p, p, p + 8, p, 1, 4, 64, 128, 0, 4, 0.1, None) == ALIGN
     assert f(p, p, p, p, p, 0, 4, 64, 128, 0, 4, 0.1, None) == OK           # empty
