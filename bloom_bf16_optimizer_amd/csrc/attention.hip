@@ -36,9 +36,10 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kAttnBlockM = 128;  // queries per workgroup (4 waves x 32)
-constexpr int kAttnBlockN = 64;   // keys per block
-constexpr int kAttnThreads = 256;
+constexpr int kAttnBlockM = 128;       // queries per workgroup (4 waves x 32)
+constexpr int kAttnBlockN = 64;        // keys per block
+constexpr int kAttnGroupThreads = 256; // one key stream: 4 waves, one per 32 queries
+constexpr int kAttnThreads = 2 * kAttnGroupThreads;  // two key streams over the same queries
 
 struct AttnSlopes {
   float s[BLOOM_MAX_HEADS];  // slope_h * log2(e)
@@ -48,65 +49,62 @@ __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b,
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-// Per-thread share of one key block in flight: 16-byte vectors of K (row
-// major) and of V (4 consecutive keys x 8 consecutive d, written to LDS
-// transposed).
+// One key block of K or V in LDS: 64 rows of D bf16, row-major, unpadded,
+// written straight from global memory by global_load_lds_dwordx4 (each lane
+// of a wave moves one 16-byte chunk to LDS address m0 + lane*16).  Within a
+// row the 16-byte chunks are XOR-swizzled so that the two read patterns are
+// free of bank conflicts:
+//  - K is read one chunk per lane down 16 consecutive rows (the A operand of
+//    the score MFMA): chunk c of row r sits at c ^ ((r / RPB) % CPR), so 16
+//    rows spread over 16 different 4-bank groups;
+//  - V is read with the transposing ds_read_b64_tr_b16, 64 bytes of each of
+//    4 consecutive rows at a time: chunk c of row r sits at
+//    c ^ 4*((r / RPB) % (CPR/4)), so those 4 rows occupy disjoint banks.
 template <int D>
-struct AttnStage {
-  static constexpr int VPR = D / 8;                                  // 16-byte vectors per row
-  static constexpr int KV = (kAttnBlockN * VPR) / kAttnThreads;      // K vectors per thread (>= 1)
-  static constexpr int VGROUPS = (kAttnBlockN / 4) * VPR;            // (4-key group, d chunk) pairs
-  uint4 kr[KV > 0 ? KV : 1];
-  uint4 vr[4];
+struct AttnTile {
+  static constexpr int CPR = D / 8;                      // 16-byte chunks per row
+  static constexpr int RPB = 16 / CPR;                   // rows per 256 bytes
+  static constexpr int CHUNKS = kAttnBlockN * CPR;       // chunks per tile
+  static constexpr int DMA = CHUNKS / kAttnGroupThreads; // transfers per lane per tile
+  static_assert(DMA >= 1 && CHUNKS % kAttnGroupThreads == 0, "tile / stream size");
+  __device__ static int swz_k(int r) { return (r / RPB) % CPR; }
+  __device__ static int swz_v(int r) { return 4 * ((r / RPB) % (CPR / 4)); }
 };
 
-template <int D>
-__device__ __forceinline__ void attn_load(AttnStage<D>& st, const uint4* __restrict__ k, const uint4* __restrict__ v,
-                                          int64_t base, int k0, int seq, int t) {
-  constexpr int VPR = AttnStage<D>::VPR;
-#pragma unroll
-  for (int r = 0; r < AttnStage<D>::KV; ++r) {
-    const int idx = t + r * kAttnThreads;
-    const int key = k0 + idx / VPR;
-    st.kr[r] = key < seq ? k[(base + key) * VPR + idx % VPR] : make_uint4(0u, 0u, 0u, 0u);
-  }
-  if (t < AttnStage<D>::VGROUPS) {
-    const int kg = t % (kAttnBlockN / 4), c = t / (kAttnBlockN / 4);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int key = k0 + 4 * kg + u;
-      st.vr[u] = key < seq ? v[(base + key) * VPR + c] : make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
+typedef __attribute__((address_space(3))) uint4 attn_lds_uint4;
+typedef unsigned int attn_u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) attn_u32x4 attn_lds_u32x4;
+typedef short attn_v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) attn_v4s attn_lds_v4s;
+
+// One 16-byte-per-lane transfer from global memory into LDS at m0 + lane*16
+// (cached: K and V are re-read by every query block of the head).
+__device__ __forceinline__ void attn_dma16(const uint4* src, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
 }
 
-template <int D>
-__device__ __forceinline__ void attn_store(const AttnStage<D>& st, uint16_t* ks, uint16_t* vt, int t) {
-  constexpr int VPR = AttnStage<D>::VPR;
-  constexpr int KROW = D + 8, VROW = kAttnBlockN + 8;
+// Requests key block [k0, k0+64) of K (SWZ_V false) or V into `tile`; this
+// wave (wq of the stream's four) moves chunks [64*(4x + wq), +64) for each
+// x.  Rows past the end of the sequence re-read row seq-1: their keys are
+// masked for every query that is stored.
+template <int D, bool SWZ_V>
+__device__ __forceinline__ void attn_request(const uint4* __restrict__ g, attn_lds_uint4* tile, int64_t base, int k0,
+                                             int seq, int wq, int lane) {
+  using T = AttnTile<D>;
 #pragma unroll
-  for (int r = 0; r < AttnStage<D>::KV; ++r) {
-    const int idx = t + r * kAttnThreads;
-    *reinterpret_cast<uint4*>(&ks[(idx / VPR) * KROW + (idx % VPR) * 8]) = st.kr[r];
-  }
-  if (t < AttnStage<D>::VGROUPS) {
-    const int kg = t % (kAttnBlockN / 4), c = t / (kAttnBlockN / 4);
-    const uint32_t w0[4] = {st.vr[0].x, st.vr[0].y, st.vr[0].z, st.vr[0].w};
-    const uint32_t w1[4] = {st.vr[1].x, st.vr[1].y, st.vr[1].z, st.vr[1].w};
-    const uint32_t w2[4] = {st.vr[2].x, st.vr[2].y, st.vr[2].z, st.vr[2].w};
-    const uint32_t w3[4] = {st.vr[3].x, st.vr[3].y, st.vr[3].z, st.vr[3].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      // d = 8c + 2e takes the low halves of the four keys' words, d + 1 the high halves
-      const uint2 lo = make_uint2(__builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u),
-                                  __builtin_amdgcn_perm(w3[e], w2[e], 0x05040100u));
-      const uint2 hi = make_uint2(__builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u),
-                                  __builtin_amdgcn_perm(w3[e], w2[e], 0x07060302u));
-      *reinterpret_cast<uint2*>(&vt[(8 * c + 2 * e) * VROW + 4 * kg]) = lo;
-      *reinterpret_cast<uint2*>(&vt[(8 * c + 2 * e + 1) * VROW + 4 * kg]) = hi;
-    }
+  for (int x = 0; x < T::DMA; ++x) {
+    const int first = (4 * x + wq) * kWave;
+    const int slot = first + lane;
+    const int r = slot / T::CPR, pc = slot % T::CPR;
+    const int c = pc ^ (SWZ_V ? T::swz_v(r) : T::swz_k(r));
+    const int key = min(k0 + r, seq - 1);
+    attn_dma16(g + (base + key) * T::CPR + c,
+               __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(tile + first)));
   }
 }
 
@@ -132,33 +130,27 @@ constexpr float kAttnLazyMax = 8.0f;
 // the second term being one number per lane per block.  DIAG: some key of
 // the block is after some query of the wave, so the causal mask applies.
 template <int D, bool DIAG>
-__device__ __forceinline__ void attn_block(AttnState<D>& st, const uint16_t* __restrict__ ksb,
-                                           const uint16_t* __restrict__ vtb, const bf16x8_t (&qf)[D / 16],
+__device__ __forceinline__ void attn_block(AttnState<D>& st, const attn_lds_uint4* __restrict__ kt_lds,
+                                           const attn_lds_uint4* __restrict__ vt_lds, const bf16x8_t (&qf)[D / 16],
                                            const bf16x8_t (&kx)[2], const bf16x8_t& qx, float scale2,
-                                           float slope2, int k0, int qi, int half, int col) {
-  constexpr int KS = D / 16, DT = D / 32, KROW = D + 8, VROW = kAttnBlockN + 8;
-  // S^T tiles: keys k0 + 32*kt + (8*(i/4) + 4*half + i%4), query col.  The two
-  // tiles' accumulation chains alternate, and the K fragments of step kk+1
-  // are read while step kk's products run.
+                                           float slope2, int k0, int qi, int half, int col, int lane) {
+  using T = AttnTile<D>;
+  constexpr int KS = D / 16, DT = D / 32;
+  // S^T tiles: keys k0 + 32*kt + (8*(i/4) + 4*half + i%4), query col.  Lane
+  // reads chunk 2*kk + half of K rows col and 32 + col (same swizzle).
   const f32x16_t zero = {};
   f32x16_t s[2];
   s[0] = mfma32(kx[0], qx, zero);
   s[1] = mfma32(kx[1], qx, zero);
-  const uint16_t* krow0 = &ksb[col * KROW + 8 * half];
-  const uint16_t* krow1 = krow0 + 32 * KROW;
-  uint4 a0 = *reinterpret_cast<const uint4*>(krow0);
-  uint4 a1 = *reinterpret_cast<const uint4*>(krow1);
+  const int sk = T::swz_k(col);
+  const attn_lds_u32x4* krow0 = reinterpret_cast<const attn_lds_u32x4*>(kt_lds) + col * T::CPR;
+  const attn_lds_u32x4* krow1 = krow0 + 32 * T::CPR;
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) {
-    uint4 n0 = a0, n1 = a1;
-    if (kk + 1 < KS) {
-      n0 = *reinterpret_cast<const uint4*>(krow0 + 16 * (kk + 1));
-      n1 = *reinterpret_cast<const uint4*>(krow1 + 16 * (kk + 1));
-    }
-    s[0] = mfma32(as_bf16x8(a0), qf[kk], s[0]);
-    s[1] = mfma32(as_bf16x8(a1), qf[kk], s[1]);
-    a0 = n0;
-    a1 = n1;
+    const int c = (2 * kk + half) ^ sk;
+    const attn_u32x4 a0 = krow0[c], a1 = krow1[c];
+    s[0] = mfma32(__builtin_bit_cast(bf16x8_t, a0), qf[kk], s[0]);
+    s[1] = mfma32(__builtin_bit_cast(bf16x8_t, a1), qf[kk], s[1]);
   }
   if (DIAG) {
 #pragma unroll
@@ -198,50 +190,82 @@ __device__ __forceinline__ void attn_block(AttnState<D>& st, const uint16_t* __r
       pf[2 * kt + i / 8][i % 8] = (__bf16)p;
     }
   st.l = l;
-  // O^T += V^T P^T over the 4 key steps of the block; the k order of step st
-  // is keys 16*st + 4*half + {0..3, 8..11} for lane half `half` (key step
-  // outer, head-dim tile inner: the DT accumulation chains alternate).
+  // O^T += V^T P^T over the 4 key steps of the block; the k order of step
+  // stp is keys 16*stp + 4*half + {0..3, 8..11} for lane half `half`.  The
+  // V^T operand comes from two transposing reads: lane L addresses 4
+  // consecutive d (d0 = 32*dt + 16*((L/16)%2) + 4*(L%4)) of key row
+  // 16*stp + 4*(L/32) + (L%16)/4 (+8 for the second read), and receives its
+  // own d = 32*dt + L%32 for the four keys the lanes of its 16-group
+  // addressed (key step outer, head-dim tile inner: the DT accumulation
+  // chains alternate).
+  const int tj = (lane & 15) >> 2, tc = lane & 3, tg = (lane >> 4) & 1;
+  const int trow = 4 * half + tj;                 // + 16*stp (+ 8)
+  const int tsv = T::swz_v(trow);                 // the same for every stp and the +8 row
+  const char __attribute__((address_space(3)))* vbytes =
+      reinterpret_cast<const char __attribute__((address_space(3)))*>(vt_lds);
 #pragma unroll
   for (int stp = 0; stp < 4; ++stp) {
-    uint4 vf[DT];
+    bf16x8_t vf[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* row = &vtb[(dt * 32 + col) * VROW + 16 * stp + 4 * half];
-      const uint2 lo = *reinterpret_cast<const uint2*>(row);
-      const uint2 hi = *reinterpret_cast<const uint2*>(row + 8);
-      vf[dt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      const int cc = (4 * dt + 2 * tg + (tc >> 1)) ^ tsv;
+      const int off = (16 * stp + trow) * (2 * D) + 16 * cc + 8 * (tc & 1);
+      const attn_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((attn_lds_v4s*)(vbytes + off));
+      const attn_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((attn_lds_v4s*)(vbytes + off + 8 * 2 * D));
+      const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
+      vf[dt] = as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
     }
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) st.oacc[dt] = mfma32(as_bf16x8(vf[dt]), pf[stp], st.oacc[dt]);
+    for (int dt = 0; dt < DT; ++dt) st.oacc[dt] = mfma32(vf[dt], pf[stp], st.oacc[dt]);
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(kAttnThreads) void attention_fwd_kernel(
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_fwd_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
     uint2* __restrict__ o, float* __restrict__ lse, int seq, int heads, int qblocks, int bh_count,
-    float scale2, AttnSlopes slopes) {
+    bool xcd_split, float scale2, AttnSlopes slopes) {
   constexpr int KS = D / 16;            // MFMA k-steps over the head dimension
   constexpr int DT = D / 32;            // 32-wide tiles of the head dimension
-  constexpr int KROW = D + 8;           // padded K row (bf16)
-  constexpr int VROW = kAttnBlockN + 8; // padded V^T row (bf16)
   constexpr int VPR = D / 8;            // 16-byte vectors per K/V row
-  // two stages of K and V^T: the next key block is stored while this one is used
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kAttnBlockN * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[2][D * VROW];
+  constexpr int CH = AttnTile<D>::CHUNKS;
+  // [stage][stream][K, V] tiles: the next pair of key blocks arrives while
+  // this pair is used.  At the end the same memory carries stream 1's
+  // partial results to stream 0.
+  __shared__ __attribute__((aligned(16))) uint4 tiles[2][2][2][CH];
+  static_assert(sizeof(tiles) >= 4 * (DT * 16 + 2) * kWave * sizeof(float), "merge area");
 
+  // Two streams of four waves take the same 128 queries (wave w and w+4 the
+  // same 32) and alternate over the key blocks, so a workgroup's serial
+  // chain is half its key blocks; their partial softmax states merge at the
+  // end.
   const int t = threadIdx.x;
   const int w = t / kWave, lane = t & (kWave - 1), half = lane >> 5, col = lane & 31;
-  // Causal work grows with the query block: the grid walks query blocks from
-  // the last (most keys) to the first, every (b, h) at each step, so the
-  // longest workgroups are dispatched first and the short ones fill the tail.
-  const int qb = qblocks - 1 - (int)(blockIdx.x / (unsigned)bh_count);
-  const int64_t bh = blockIdx.x % (unsigned)bh_count;
+  const int stream = w >> 2, wq = w & 3;
+  // Causal work grows with the query block, so the longest workgroups are
+  // dispatched first and the short ones fill the tail.  Workgroup i runs on
+  // XCD i % 8, and each XCD has its own L2: with xcd_split, every (b, h) is
+  // cut into its even and odd query blocks, XCD x takes half-heads
+  // [x*n, (x+1)*n) and walks them heaviest query block first, so an XCD's L2
+  // holds the K and V of at most n/2 + 1 heads.  Otherwise the grid walks
+  // query blocks from the last to the first, every (b, h) at each step.
+  int qb;
+  int64_t bh;
+  if (xcd_split) {
+    const int x = (int)(blockIdx.x % 8u), j = (int)(blockIdx.x / 8u);
+    const int n = bh_count / 4;  // half-heads per XCD
+    const int rank = j / n, hh = n * x + j % n, par = hh & 1;
+    bh = hh >> 1;
+    qb = qblocks - 1 - ((qblocks - 1 - par) & 1) - 2 * rank;
+  } else {
+    qb = qblocks - 1 - (int)(blockIdx.x / (unsigned)bh_count);
+    bh = blockIdx.x % (unsigned)bh_count;
+  }
   const int h = (int)(bh % heads);
   const float slope2 = slopes.s[h];
   const int64_t base = bh * (int64_t)seq;  // row index of (b, h, 0)
-  const int q0 = qb * kAttnBlockM + w * 32;  // this wave's first query
-  const int qi = q0 + col;                   // this lane's query
+  const int q0 = qb * kAttnBlockM + wq * 32;  // this wave's first query
+  const int qi = q0 + col;                    // this lane's query
   const bool qvalid = qi < seq;
   const bool wave_live = q0 < seq;
 
@@ -280,29 +304,66 @@ __global__ __launch_bounds__(kAttnThreads) void attention_fwd_kernel(
   st.m = -INFINITY;
   st.l = 0.f;
 
-  // Key blocks run from the diagonal back to key 0: the block holding a
-  // row's own key comes first, and with the ALiBi bias falling off with
-  // distance the running max then rarely moves.
+  // Key blocks run from the diagonal back to key 0 (stream s takes blocks
+  // nkb-1-s, nkb-3-s, ...): the block holding a row's own key comes first,
+  // and with the ALiBi bias falling off with distance the running max then
+  // rarely moves.
   const int wg_last_q = min(seq, (qb + 1) * kAttnBlockM) - 1;
   const int nkb = wg_last_q / kAttnBlockN + 1;
-  AttnStage<D> stage;
-  attn_load<D>(stage, k, v, base, (nkb - 1) * kAttnBlockN, seq, t);
-  attn_store<D>(stage, ks[0], vt[0], t);
+  const int iters = (nkb + 1) / 2;
+  attn_lds_uint4* lt = (attn_lds_uint4*)&tiles[0][0][0][0];
+  auto tile = [&](int stage, int which) { return lt + ((stage * 2 + stream) * 2 + which) * CH; };
+  int kb = nkb - 1 - stream;
+  if (kb >= 0) {
+    attn_request<D, false>(k, tile(0, 0), base, kb * kAttnBlockN, seq, wq, lane);
+    attn_request<D, true>(v, tile(0, 1), base, kb * kAttnBlockN, seq, wq, lane);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int kb = nkb - 1, buf = 0; kb >= 0; --kb, buf ^= 1) {
+  for (int it = 0, buf = 0; it < iters; ++it, buf ^= 1, kb -= 2) {
     const int k0 = kb * kAttnBlockN;
-    // next block's loads are in flight during this block's products
-    if (kb > 0) attn_load<D>(stage, k, v, base, k0 - kAttnBlockN, seq, t);
+    // the next block's transfers run during this block's products (the
+    // barrier that ended the previous iteration freed their buffer)
+    if (kb >= 2) {
+      attn_request<D, false>(k, tile(buf ^ 1, 0), base, k0 - 2 * kAttnBlockN, seq, wq, lane);
+      attn_request<D, true>(v, tile(buf ^ 1, 1), base, k0 - 2 * kAttnBlockN, seq, wq, lane);
+    }
     // Every processed block has k0 <= q0 (both are multiples of 32), so each
     // row has its key k0 unmasked and the first block sets a finite max.
-    if (wave_live && k0 <= q0 + 31) {
+    if (kb >= 0 && wave_live && k0 <= q0 + 31) {
       if (k0 + kAttnBlockN - 1 > q0)
-        attn_block<D, true>(st, ks[buf], vt[buf], qf, kx, qx, scale2, slope2, k0, qi, half, col);
+        attn_block<D, true>(st, tile(buf, 0), tile(buf, 1), qf, kx, qx, scale2, slope2, k0, qi, half, col, lane);
       else
-        attn_block<D, false>(st, ks[buf], vt[buf], qf, kx, qx, scale2, slope2, k0, qi, half, col);
+        attn_block<D, false>(st, tile(buf, 0), tile(buf, 1), qf, kx, qx, scale2, slope2, k0, qi, half, col, lane);
     }
-    if (kb > 0) attn_store<D>(stage, ks[buf ^ 1], vt[buf ^ 1], t);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  }
+
+  // Merge stream 1 into stream 0 through LDS ([wave][value][lane] floats).
+  // Block 0 is processed by one of the streams for every live row, so at
+  // least one of the two maxima is finite.
+  float* mg = reinterpret_cast<float*>(&tiles[0][0][0][0]) + wq * (DT * 16 + 2) * kWave + lane;
+  if (stream == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mg[(dt * 16 + i) * kWave] = st.oacc[dt][i];
+    mg[(DT * 16) * kWave] = st.m;
+    mg[(DT * 16 + 1) * kWave] = st.l;
+  }
+  __syncthreads();
+  if (stream == 1) return;
+  {
+    const float m1 = mg[(DT * 16) * kWave], l1 = mg[(DT * 16 + 1) * kWave];
+    const float m = fmaxf(st.m, m1);
+    const float a0 = __builtin_amdgcn_exp2f(st.m - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.oacc[dt][i] = fmaf(st.oacc[dt][i], a0, mg[(dt * 16 + i) * kWave] * a1);
+    st.l = fmaf(st.l, a0, l1 * a1);
+    st.m = m;
   }
 
   // Normalise: the two lane halves hold the sums over complementary keys.
@@ -366,6 +427,8 @@ extern "C" bloom_status bloom_alibi_attention_fwd(const bloom_bf16* q, const blo
   const float scale2 = (float)((double)scale * log2e);
   const int qblocks = (int)((seq + kAttnBlockM - 1) / kAttnBlockM);
   const dim3 grid((unsigned)(batch * heads * qblocks));
+  // whole half-heads per XCD: an even number of query blocks, (b, h) pairs a multiple of 4
+  const bool xcd_split = qblocks % 2 == 0 && (batch * heads) % 4 == 0;
   const uint4* qv = reinterpret_cast<const uint4*>(q);
   const uint4* kv = reinterpret_cast<const uint4*>(k);
   const uint4* vv = reinterpret_cast<const uint4*>(v);
@@ -373,15 +436,15 @@ extern "C" bloom_status bloom_alibi_attention_fwd(const bloom_bf16* q, const blo
   switch (head_dim) {
     case 32:
       hipLaunchKernelGGL((attention_fwd_kernel<32>), grid, dim3(kAttnThreads), 0, stream, qv, kv, vv, ov, lse,
-                         (int)seq, (int)heads, qblocks, (int)(batch * heads), scale2, table);
+                         (int)seq, (int)heads, qblocks, (int)(batch * heads), xcd_split, scale2, table);
       break;
     case 64:
       hipLaunchKernelGGL((attention_fwd_kernel<64>), grid, dim3(kAttnThreads), 0, stream, qv, kv, vv, ov, lse,
-                         (int)seq, (int)heads, qblocks, (int)(batch * heads), scale2, table);
+                         (int)seq, (int)heads, qblocks, (int)(batch * heads), xcd_split, scale2, table);
       break;
     default:
       hipLaunchKernelGGL((attention_fwd_kernel<128>), grid, dim3(kAttnThreads), 0, stream, qv, kv, vv, ov, lse,
-                         (int)seq, (int)heads, qblocks, (int)(batch * heads), scale2, table);
+                         (int)seq, (int)heads, qblocks, (int)(batch * heads), xcd_split, scale2, table);
       break;
   }
   return launch_status("bloom_alibi_attention_fwd");
