@@ -79,32 +79,39 @@ typedef __attribute__((address_space(3))) attn_u32x4 attn_lds_u32x4;
 typedef short attn_v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) attn_v4s attn_lds_v4s;
 
-// One 16-byte-per-lane transfer from global memory into LDS at m0 + lane*16
-// (cached: K and V are re-read by every query block of the head).
-__device__ __forceinline__ void attn_dma16(const uint4* src, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+// One 16-byte-per-lane transfer from global memory (wave-uniform base plus
+// a 32-bit byte offset per lane) into LDS at m0 + lane*16 (cached: K and V
+// are re-read by every query block of the head).
+__device__ __forceinline__ void attn_dma16(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(src), "s"(m0)
+               : "v"(voff), "s"(sbase), "s"(m0)
                : "memory", "m0");
 }
 
 // Requests key block [k0, k0+64) of K (SWZ_V false) or V into `tile`; this
 // wave (wq of the stream's four) moves chunks [64*(4x + wq), +64) for each
-// x.  Rows past the end of the sequence re-read row seq-1: their keys are
-// masked for every query that is stored.
+// x.  A lane's chunk offset within the block does not depend on k0 (so it
+// stays in a register across blocks); only the block at the end of the
+// sequence re-reads row seq-1 for its rows past the end (their keys are
+// masked for every query that is stored).
 template <int D, bool SWZ_V>
 __device__ __forceinline__ void attn_request(const uint4* __restrict__ g, attn_lds_uint4* tile, int64_t base, int k0,
                                              int seq, int wq, int lane) {
   using T = AttnTile<D>;
+  const uint64_t gp = (uint64_t)(uintptr_t)(g + (base + k0) * T::CPR);
+  const uint4* gb = (const uint4*)(uintptr_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(gp >> 32)) << 32) |
+                                               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)gp));
+  const bool tail = k0 + kAttnBlockN > seq;  // wave-uniform
 #pragma unroll
   for (int x = 0; x < T::DMA; ++x) {
     const int first = (4 * x + wq) * kWave;
     const int slot = first + lane;
     const int r = slot / T::CPR, pc = slot % T::CPR;
     const int c = pc ^ (SWZ_V ? T::swz_v(r) : T::swz_k(r));
-    const int key = min(k0 + r, seq - 1);
-    attn_dma16(g + (base + key) * T::CPR + c,
-               __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(tile + first)));
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(tile + first));
+    const int row = tail ? min(r, seq - 1 - k0) : r;
+    attn_dma16(gb, (uint32_t)(row * T::CPR + c) * 16u, m0);
   }
 }
 
