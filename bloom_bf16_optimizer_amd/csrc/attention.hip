@@ -81,7 +81,9 @@ typedef __attribute__((address_space(3))) attn_v4s attn_lds_v4s;
 
 // One 16-byte-per-lane transfer from global memory (wave-uniform base plus
 // a 32-bit byte offset per lane) into LDS at m0 + lane*16 (cached: K and V
-// are re-read by every query block of the head).
+// are re-read by every query block of the head).  m0 is written only here:
+// the compiler uses it for nothing else in this kernel (checked in the
+// generated code), so the clobber is only a precaution.
 __device__ __forceinline__ void attn_dma16(const void* sbase, uint32_t voff, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
