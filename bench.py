@@ -227,8 +227,18 @@ def run_gpu(args):
         return lambda: ops.bloom_alibi_attention_fwd(q, k, v, o, lse, X.softmax.head_offset, X.softmax.total_heads,
                                                      scale)
 
+    L = W.LONG.softmax  # the 8192-token extrapolation shape, 28 heads
+
+    def att_fwd_long_set(s):
+        q = fill((L.batch, L.heads, L.seq, L.head_dim), W.S_ATT_Q, 1.0, s=s)
+        k = fill((L.batch, L.heads, L.seq, L.head_dim), W.S_ATT_K, 1.0, s=s)
+        v = fill((L.batch, L.heads, L.seq, L.head_dim), W.S_ATT_V, 1.0, s=s)
+        o = torch.empty_like(q)
+        lse = torch.empty((L.batch, L.heads, L.seq), dtype=f32, device=dev)
+        return lambda: ops.bloom_alibi_attention_fwd(q, k, v, o, lse, L.head_offset, L.total_heads, L.scale)
+
     sweep_only = [("layernorm_residual_fwd", lnr_fwd_set, 4), ("layernorm_residual_bwd", lnr_bwd_set, 4),
-                  ("alibi_attention_fwd", att_fwd_set, 4)]
+                  ("alibi_attention_fwd", att_fwd_set, 4), ("alibi_attention_fwd_8192", att_fwd_long_set, 2)]
 
     log(f"bench: allocating the shard workload (n = {n:,}, {GRAD_BUFFERS} gradient buffers)")
     master = fill((n,), W.S_OPT_PARAM, W.PARAM_SIGMA, dtype=f32)
@@ -315,7 +325,11 @@ def run_gpu(args):
         sweep[name] = a.elapsed_time(b) / reps
         del fns
     shapes = {"ln": (rows, hid), "sm": (smb, smh, sms), "gelu": (grows, gcols), "head_dim": hd}
-    return ms_step, in_step, sweep, bytes_model(shapes, n, mb), n, mb
+    bts = bytes_model(shapes, n, mb)
+    lb, lh, ls, ld = L.batch, L.heads, L.seq, L.head_dim
+    bts["alibi_attention_fwd_8192"] = lb * lh * ls * ld * 2 * 4 + lb * lh * ls * 4
+    bts["_attention_flops_8192"] = 2 * 2 * lb * lh * (ls * (ls + 1) // 2) * ld
+    return ms_step, in_step, sweep, bts, n, mb
 
 
 # ----------------------------------------------------------------------------
@@ -421,13 +435,15 @@ def main():
                       else "events around each launch in the timed steps"}
         if k in sweep:
             kernels[k]["in_step_ms"] = round(in_step[k], 4) if k in in_step else None
-    if "alibi_attention_fwd" in kernels:
+    for att, fk in (("alibi_attention_fwd", "_attention_flops"), ("alibi_attention_fwd_8192", "_attention_flops_8192")):
+        if att not in kernels:
+            continue
         # causal: q.k and p.v each take 2*D flops for every (query, key <= query) pair
-        flops = bts["_attention_flops"]
-        tf = flops / (per["alibi_attention_fwd"] * 1e-3) / 1e12
-        kernels["alibi_attention_fwd"].update({"flops": flops, "TFLOP/s": round(tf, 1),
-                                               "frac_of_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                                               "bound": "mfma (bf16 dense, 2500 TFLOP/s)"})
+        flops = bts[fk]
+        tf = flops / (per[att] * 1e-3) / 1e12
+        kernels[att].update({"flops": flops, "TFLOP/s": round(tf, 1),
+                             "frac_of_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "bound": "mfma (bf16 dense, 2500 TFLOP/s)"})
     dom = "grad_accumulate"
     dom_gbs = bts[dom] / (per[dom] * 1e-3) / 1e9
     traffic = measured_traffic(dom)
