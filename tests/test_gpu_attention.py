@@ -67,9 +67,12 @@ def test_attention_long_context_sampled():
 
 
 # seq not a multiple of the 128-query or 64-key blocks; head_offset inside a
-# larger model; every head dimension.
+# larger model; every head dimension.  (1,4,200,64) and (2,2,392,128) have an
+# even number of query blocks and (b, h) pairs a multiple of 4, so they take
+# the XCD-split workgroup order with a ragged last block.
 @pytest.mark.parametrize("b,h,s,d,off,tot", [(1, 1, 8, 32, 0, 1), (2, 3, 24, 64, 5, 12), (1, 2, 136, 128, 0, 112),
-                                            (1, 2, 200, 64, 100, 112), (3, 1, 72, 32, 3, 6), (1, 1, 264, 128, 0, 16)])
+                                            (1, 2, 200, 64, 100, 112), (3, 1, 72, 32, 3, 6), (1, 1, 264, 128, 0, 16),
+                                            (1, 4, 200, 64, 8, 112), (2, 2, 392, 128, 0, 2)])
 def test_attention_ragged(b, h, s, d, off, tot):
     require_gpu()
     q, k, v = _inputs(41, b, h, s, d)
