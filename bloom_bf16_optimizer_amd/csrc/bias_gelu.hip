@@ -32,7 +32,7 @@ namespace {
 constexpr double kKd = 0.7978845608028654;
 constexpr double kCd = 0.044715;
 constexpr double kLog2e = 1.4426950408889634;
-constexpr int kFwdRows = 4;                              // rows per forward strip
+constexpr int kFwdRows = 2;                              // rows per forward strip
 constexpr int kBwdStageRows = 2;                         // rows per backward stage
 constexpr int kBwdStages = 4;                            // stages per wave
 constexpr int kBwdRowsPerWave = kBwdStageRows * kBwdStages;
