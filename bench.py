@@ -6,13 +6,17 @@ data already resident in HBM:
   LayerNorm fwd + bwd          [2048, 14336] bf16
   ALiBi causal softmax fwd+bwd [1, 28, 2048, 2048] bf16 (heads 0..27 of 112)
   bias + GeLU fwd + bwd        [2048, 14336] bf16
-  FP32 gradient accumulation   32 micro-batches of a 3.67e9-element bf16 gradient
+  FP32 gradient accumulation   32 micro-batches of a 3.67e9-element bf16 gradient,
+                               8 resident micro-batch gradients added per pass
   BF16Optimizer step           global norm, clip 1.0, AdamW, bf16 parameter copy
 
 Each kernel reads inputs that were last touched a whole step earlier (the
 accumulation streams ~1.2 TB per step in between), so no kernel is served by
 the 256 MB Infinity Cache from the previous one.  The 32 micro-batch gradients
 cycle through GRAD_BUFFERS distinct 7.34 GB buffers (all 32 would need 235 GB).
+By default each accumulation pass adds `--accum-batch` (8) of them to the FP32
+accumulator in micro-batch order (4 passes of 24 B per element instead of 32 of
+10 B, bit-identical); `--accum-batch 1` times one pass per micro-batch.
 
 Prints one JSON line.  `value` is the whole step's algorithmic HBM throughput
 (sum of each kernel's algorithmic bytes / step time, GB/s); per-kernel
@@ -51,7 +55,7 @@ def log(*a):
 
 # ----------------------------------------------------------------------------
 # Algorithmic bytes of each step row (what the method must read and write).
-def bytes_model(sh, n, mb):
+def bytes_model(sh, n, mb, batch=GRAD_BUFFERS):
     rows, hid = sh["ln"]
     b, h, s = sh["sm"]
     live = b * h * s * (s + 1) // 2          # causal entries read
@@ -74,6 +78,10 @@ def bytes_model(sh, n, mb):
         "grad_accumulate_first": n * 6,
         "grad_accumulate": n * 10,
         "grad_accumulate_last": n * 10,  # also emits the norm's FP64 partials (1/1024 of a double per element)
+        # `batch` resident micro-batch gradients per pass: read them once, read + write acc once
+        "grad_accumulate_many_first": n * (2 * batch + 4),
+        "grad_accumulate_many": n * (2 * batch + 8),
+        "grad_accumulate_many_last": n * (2 * batch + 8),
         "adamw_step": n * 30,   # update reads acc, master, m, v (16 B), writes master, m, v, bf16 (14 B)
     }
 
@@ -125,6 +133,7 @@ def run_gpu(args):
     O = W.OPTIMIZER
     n = O.opt.n if args.n is None else args.n
     mb = O.opt.microbatches
+    batch = args.accum_batch
     rows, hid = X.ln.rows, X.ln.hidden
     smb, smh, sms = X.softmax.batch, X.softmax.heads, X.softmax.seq
     grows, gcols = X.gelu.rows, X.gelu.cols
@@ -237,8 +246,14 @@ def run_gpu(args):
         lse = torch.empty((L.batch, L.heads, L.seq), dtype=f32, device=dev)
         return lambda: ops.bloom_alibi_attention_fwd(q, k, v, o, lse, L.head_offset, L.total_heads, L.scale)
 
+    def acc_one_set(s):
+        # one micro-batch per pass (a later micro-batch), over the resident gradient buffers
+        return lambda: ops.bloom_bf16_grad_accumulate(acc, grads[s], False)
+
     sweep_only = [("layernorm_residual_fwd", lnr_fwd_set, 4), ("layernorm_residual_bwd", lnr_bwd_set, 4),
                   ("alibi_attention_fwd", att_fwd_set, 4), ("alibi_attention_fwd_8192", att_fwd_long_set, 2)]
+    if batch > 1:
+        sweep_only.append(("grad_accumulate", acc_one_set, GRAD_BUFFERS))
 
     log(f"bench: allocating the shard workload (n = {n:,}, {GRAD_BUFFERS} gradient buffers)")
     master = fill((n,), W.S_OPT_PARAM, W.PARAM_SIGMA, dtype=f32)
@@ -252,8 +267,11 @@ def run_gpu(args):
     torch.cuda.synchronize()
     log(f"bench: resident {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
 
-    names = [name for name, _ in step_fused] + ["grad_accumulate_first", "grad_accumulate", "grad_accumulate_last",
-                                                "adamw_step"]
+    if batch == 1:
+        acc_names = ["grad_accumulate_first", "grad_accumulate", "grad_accumulate_last"]
+    else:
+        acc_names = ["grad_accumulate_many_first", "grad_accumulate_many", "grad_accumulate_many_last"]
+    names = [name for name, _ in step_fused] + acc_names + ["adamw_step"]
     ev = {k: [] for k in names}
 
     def timed(name, fn, record):
@@ -270,14 +288,23 @@ def run_gpu(args):
     def step(t, record):
         for name, fn in step_fused:
             timed(name, fn, record)
-        for k in range(mb):
-            g = grads[k % GRAD_BUFFERS]
-            if k == mb - 1:   # the last micro-batch also writes the norm's partial sums
-                timed("grad_accumulate_last", lambda g=g, k=k: ops.bloom_bf16_grad_accumulate_sumsq(
-                    acc, g, k == 0, opt_ws), record)
-            else:
-                name = "grad_accumulate_first" if k == 0 else "grad_accumulate"
-                timed(name, lambda g=g, k=k: ops.bloom_bf16_grad_accumulate(acc, g, k == 0), record)
+        if batch == 1:
+            for k in range(mb):
+                g = grads[k % GRAD_BUFFERS]
+                if k == mb - 1:   # the last micro-batch also writes the norm's partial sums
+                    timed("grad_accumulate_last", lambda g=g, k=k: ops.bloom_bf16_grad_accumulate_sumsq(
+                        acc, g, k == 0, opt_ws), record)
+                else:
+                    name = "grad_accumulate_first" if k == 0 else "grad_accumulate"
+                    timed(name, lambda g=g, k=k: ops.bloom_bf16_grad_accumulate(acc, g, k == 0), record)
+        else:
+            for k0 in range(0, mb, batch):
+                group = [grads[(k0 + j) % GRAD_BUFFERS] for j in range(batch)]
+                last = k0 + batch == mb    # the last pass also writes the norm's partial sums
+                name = ("grad_accumulate_many_first" if k0 == 0 else
+                        "grad_accumulate_many_last" if last else "grad_accumulate_many")
+                timed(name, lambda group=group, k0=k0, last=last: ops.bloom_bf16_grad_accumulate_many(
+                    acc, group, k0 == 0, opt_ws if last else None), record)
         hp = ops.adamw_hparams(W.LR, W.BETA1, W.BETA2, W.ADAM_EPS, W.WEIGHT_DECAY, W.MAX_GRAD_NORM, t,
                                sumsq_in_workspace=True)
         timed("adamw_step", lambda: ops.bloom_bf16_adamw_step(master, exp_avg, exp_avg_sq, param, acc, hp, norm,
@@ -325,7 +352,7 @@ def run_gpu(args):
         sweep[name] = a.elapsed_time(b) / reps
         del fns
     shapes = {"ln": (rows, hid), "sm": (smb, smh, sms), "gelu": (grows, gcols), "head_dim": hd}
-    bts = bytes_model(shapes, n, mb)
+    bts = bytes_model(shapes, n, mb, batch)
     lb, lh, ls, ld = L.batch, L.heads, L.seq, L.head_dim
     bts["alibi_attention_fwd_8192"] = lb * lh * ls * ld * 2 * 4 + lb * lh * ls * 4
     bts["_attention_flops_8192"] = 2 * 2 * lb * lh * (ls * (ls + 1) // 2) * ld
@@ -411,21 +438,32 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run 3 plain 1 GiB device-to-device copies (counter calibration)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the per-kernel sweep of the fused kernels")
+    ap.add_argument("--accum-batch", type=int, default=GRAD_BUFFERS,
+                    help="resident micro-batch gradients added per accumulation pass (1 = one pass each)")
     args = ap.parse_args()
+    if not (1 <= args.accum_batch <= GRAD_BUFFERS) or (args.accum_batch > 1 and 32 % (2 * args.accum_batch)):
+        print(f"--accum-batch must be 1 or divide the 32 micro-batches into at least two passes of at most "
+              f"{GRAD_BUFFERS}", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the hot path runs on a single MI355X at one GPU's shard shape, "
               "and runs on several GPUs are not supported.", file=sys.stderr)
         sys.exit(2)
 
     ms_step, in_step, sweep, bts, n, mb = run_gpu(args)
+    batch = args.accum_batch
     per = dict(in_step)
     per.update(sweep)
     sweep = sweep or {}
     nfirst, nrest = 1, mb - 2
-    step_bytes = (sum(bts[k] for k in ("layernorm_fwd", "layernorm_bwd", "alibi_softmax_fwd",
-                                       "alibi_softmax_bwd", "bias_gelu_fwd", "bias_gelu_bwd", "adamw_step",
-                                       "grad_accumulate_last"))
-                  + nfirst * bts["grad_accumulate_first"] + nrest * bts["grad_accumulate"])
+    step_bytes = sum(bts[k] for k in ("layernorm_fwd", "layernorm_bwd", "alibi_softmax_fwd", "alibi_softmax_bwd",
+                                      "bias_gelu_fwd", "bias_gelu_bwd", "adamw_step"))
+    if batch == 1:
+        step_bytes += (bts["grad_accumulate_last"] + nfirst * bts["grad_accumulate_first"]
+                       + nrest * bts["grad_accumulate"])
+    else:
+        step_bytes += (bts["grad_accumulate_many_first"] + bts["grad_accumulate_many_last"]
+                       + (mb // batch - 2) * bts["grad_accumulate_many"])
     kernels = {}
     for k, ms in per.items():
         gbs = bts[k] / (ms * 1e-3) / 1e9
@@ -444,7 +482,9 @@ def main():
         kernels[att].update({"flops": flops, "TFLOP/s": round(tf, 1),
                              "frac_of_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                              "bound": "mfma (bf16 dense, 2500 TFLOP/s)"})
-    dom = "grad_accumulate"
+    dom = "grad_accumulate" if batch == 1 else "grad_accumulate_many"
+    dom_label = ("grad_accumulate (micro-batches 2-31)" if batch == 1 else
+                 f"grad_accumulate_many ({batch} micro-batches per pass, passes 2-{mb // batch - 1})")
     dom_gbs = bts[dom] / (per[dom] * 1e-3) / 1e9
     traffic = measured_traffic(dom)
     result = {
@@ -465,10 +505,11 @@ def main():
                                f"bf16-optimizer over a {n}-element shard with {mb} fp32-accumulated micro-batch "
                                "gradients, global-norm clip 1.0, adamw, rne bf16 copy",
                    "optimizer_elements": n, "microbatches": mb, "grad_buffers": GRAD_BUFFERS,
+                   "microbatches_per_accumulation_pass": batch,
                    "storage": "bf16 activations and gradients, fp32 master/moments/accumulator"},
         "adamw_step_ms": round(per["adamw_step"], 3),
         "kernels": kernels,
-        "roofline": {"kernel": "grad_accumulate (micro-batches 2-31)", "bound": "hbm",
+        "roofline": {"kernel": dom_label, "bound": "hbm",
                      "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic},

@@ -57,6 +57,8 @@ SIGNATURES = {
     "bloom_bf16_adamw_workspace_size": (c_size, [c_i64]),
     "bloom_bf16_grad_accumulate_sumsq": (ctypes.c_int, [c_void_p, c_void_p, c_i64, c_i32, c_void_p, c_size,
                                                         c_void_p]),
+    "bloom_bf16_grad_accumulate_many": (ctypes.c_int, [c_void_p, ctypes.POINTER(c_void_p), c_i32, c_i64, c_i32,
+                                                       c_void_p, c_size, c_void_p]),
     "bloom_bf16_adamw_step": (ctypes.c_int, [c_void_p] * 5 + [c_i64, ctypes.POINTER(AdamWHParams), c_void_p,
                                              c_void_p, c_size, c_void_p]),
     "bloom_bf16_adamw_step_segments": (ctypes.c_int, [c_void_p] * 5 + [c_i64, ctypes.POINTER(AdamWHParams),

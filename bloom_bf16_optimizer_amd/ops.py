@@ -206,6 +206,22 @@ def bloom_bf16_grad_accumulate_sumsq(grad_acc, grad, first_microbatch: bool, wor
         _ptr(workspace, workspace.dtype, "workspace"), wsb, _stream()))
 
 
+def bloom_bf16_grad_accumulate_many(grad_acc, grads, first_microbatch: bool, workspace=None) -> None:
+    """grad_acc accumulates the bf16 tensors of `grads` in order (one pass)."""
+    grads = list(grads)
+    for k, g in enumerate(grads):
+        if g.numel() != grad_acc.numel():
+            raise ValueError(f"grads[{k}] and grad_acc must have the same number of elements")
+    arr = (ctypes.c_void_p * max(len(grads), 1))(*[_ptr(g, BF16, f"grads[{k}]") for k, g in enumerate(grads)])
+    wptr, wsb = None, 0
+    if workspace is not None:
+        wptr, wsb = _ptr(workspace, workspace.dtype, "workspace"), workspace.numel() * workspace.element_size()
+    lib = _lib.load()
+    check("bloom_bf16_grad_accumulate_many", lib.bloom_bf16_grad_accumulate_many(
+        _ptr(grad_acc, F32, "grad_acc"), arr, len(grads), grad_acc.numel(), int(bool(first_microbatch)), wptr, wsb,
+        _stream()))
+
+
 def bloom_bf16_adamw_workspace_size(n: int) -> int:
     return _lib.load().bloom_bf16_adamw_workspace_size(n)
 

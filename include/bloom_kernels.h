@@ -68,6 +68,7 @@ const char* bloom_last_error(void);
 #define BLOOM_MAX_HIDDEN 65536
 #define BLOOM_MAX_SEQ 16384
 #define BLOOM_MAX_HEADS 256
+#define BLOOM_MAX_ACCUM_BATCH 8
 
 /* ---------------------------------------------------------------------------
  * LayerNorm forward.  [overview] "融合 CUDA 核" (the fused LayerNorm kernel)
@@ -253,6 +254,28 @@ typedef struct {
 bloom_status bloom_bf16_grad_accumulate_sumsq(float* grad_acc, const bloom_bf16* grad, int64_t n,
                                               int32_t first_microbatch, void* workspace,
                                               size_t workspace_bytes, hipStream_t stream);
+
+/* Stage 1 over several micro-batches in one pass.  [overview] "BF16 优化器"
+ * (FP32 accumulation across micro-batches); [3d] 3.3 (32 accumulation steps).
+ * grad_acc accumulates grads[0], grads[1], ..., grads[count-1] in that order,
+ * each with one FP32 add exactly as bloom_bf16_grad_accumulate does (the
+ * result is bit-identical to `count` such calls), while grad_acc is read and
+ * written once instead of `count` times: for callers that keep several
+ * micro-batch gradients of the shard resident.
+ *   first_microbatch != 0: grads[0] starts the accumulation (grad_acc is only
+ *   written).
+ * grads: host array of `count` device pointers, 1 <= count <=
+ * BLOOM_MAX_ACCUM_BATCH, each [n] bf16 and 16-byte aligned (the array itself
+ * is read during the call only).  workspace: NULL, or a workspace of at least
+ * bloom_bf16_adamw_workspace_size(n) bytes, into which the norm's partial sums
+ * of the final grad_acc^2 are written as bloom_bf16_grad_accumulate_sumsq
+ * does (then pass hp->sumsq_in_workspace = 1 to the step).  Errors: count out
+ * of range or n out of range -> BLOOM_ERR_SHAPE; a NULL array or pointer ->
+ * BLOOM_ERR_NULL; misaligned -> BLOOM_ERR_ALIGN; a short workspace ->
+ * BLOOM_ERR_WORKSPACE. */
+bloom_status bloom_bf16_grad_accumulate_many(float* grad_acc, const bloom_bf16* const* grads, int32_t count,
+                                             int64_t n, int32_t first_microbatch, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace bloom_bf16_adamw_step needs (norm partials and the
  * clip coefficient). */

@@ -52,7 +52,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.bloom_abi_version() == 5
+    assert lib.bloom_abi_version() == 6
     assert lib.bloom_status_string(0) == b"ok"
     assert lib.bloom_status_string(4) == b"workspace too small"
     assert lib.bloom_status_string(99) == b"unknown status"
@@ -170,6 +170,17 @@ def test_optimizer_validation(lib):
     assert acc(p, p, -1, 1, None) == SHAPE
     assert acc(p, None, 10, 1, None) == NULL
     assert acc(p, p, 0, 0, None) == OK
+    many = lib.bloom_bf16_grad_accumulate_many
+    ptrs = (ctypes.c_void_p * 9)(*([p] * 9))
+    assert many(p, ptrs, 0, 1000, 1, None, 0, None) == SHAPE                # no micro-batch
+    assert many(p, ptrs, 9, 1000, 1, None, 0, None) == SHAPE                # more than BLOOM_MAX_ACCUM_BATCH
+    assert many(p, None, 2, 1000, 1, None, 0, None) == NULL
+    assert many(p, (ctypes.c_void_p * 2)(p, None), 2, 1000, 1, None, 0, None) == NULL
+    assert many(p, (ctypes.c_void_p * 2)(p, p + 8), 2, 1000, 1, None, 0, None) == ALIGN
+    assert many(p + 4, ptrs, 2, 1000, 1, None, 0, None) == ALIGN
+    assert many(p, ptrs, 2, 1000, 1, p, ws - 8, None) == WORKSPACE
+    assert many(p, ptrs, 2, -1, 1, None, 0, None) == SHAPE
+    assert many(p, ptrs, 2, 0, 1, None, 0, None) == OK                      # empty: nothing enqueued
 
 
 def test_adamw_segments_validation(lib):

@@ -135,6 +135,43 @@ def test_fused_norm_partials_match_standalone(n, mb):
     assert abs(float(outs[1][5][0]) - ref) <= 1e-6 * ref
 
 
+@pytest.mark.parametrize("n,mb,batch", [(1_000_003, 11, 4), (4099, 8, 8), (7, 3, 2), (100_000, 32, 8), (1, 1, 1),
+                                        (3_000_000, 5, 3)])
+def test_accumulate_many_bit_exact(n, mb, batch):
+    """Several micro-batches per pass (groups of `batch`, the last possibly
+    shorter): bit-identical to one pass per micro-batch and to the oracle's
+    sequential FP32 adds; the last group with the norm partials gives the
+    same step as the standalone norm."""
+    require_gpu()
+    seed = 7
+    grads = []
+    for k in range(mb):
+        g = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        sdev.fill_(g, seed, W.S_OPT_GRAD0 + 1 + k, W.GRAD_SIGMA)
+        grads.append(g)
+    ws = _workspace(n)
+    acc = torch.empty(n, dtype=torch.float32, device="cuda")
+    for k0 in range(0, mb, batch):
+        group = grads[k0:k0 + batch]
+        last = k0 + batch >= mb
+        ops.bloom_bf16_grad_accumulate_many(acc, group, k0 == 0, ws if last else None)
+    torch.cuda.synchronize()
+    got = acc.cpu().numpy()
+    ref = _accumulate_oracle(np.arange(n, dtype=np.uint64), seed, mb)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), "accumulator not bit-exact"
+    single = _accumulate_gpu(n, seed, mb).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), single.view(np.uint32))
+    outs = []
+    for fused in (True, False):
+        tp = gen((n,), seed, W.S_OPT_PARAM, W.PARAM_SIGMA, dtype=torch.float32)[0]
+        tm = torch.zeros(n, dtype=torch.float32, device="cuda")
+        tv = torch.zeros(n, dtype=torch.float32, device="cuda")
+        param, norm = _step_gpu(tp, tm, tv, acc, _hp(1, sumsq_in_workspace=fused), ws=ws if fused else None)
+        outs.append((tp.cpu().numpy(), host_bf16(param), norm))
+    assert np.array_equal(outs[0][0].view(np.uint32), outs[1][0].view(np.uint32))
+    assert np.array_equal(outs[0][1], outs[1][1]) and outs[0][2] == outs[1][2]
+
+
 def test_two_steps_and_checkpoint_round_trip():
     """t = 1 then t = 2; a host round trip of the state between steps (the
     checkpoint analogue) continues bit-identically."""
