@@ -50,6 +50,9 @@ SIGNATURES = {
                                                c_void_p]),
     "bloom_alibi_attention_fwd": (ctypes.c_int, [c_void_p] * 5 + [c_i64, c_i32, c_i64, c_i32, c_i32, c_i32, c_f32,
                                                  c_void_p]),
+    "bloom_alibi_attention_bwd_workspace_size": (c_size, [c_i64, c_i32, c_i64]),
+    "bloom_alibi_attention_bwd": (ctypes.c_int, [c_void_p] * 8 + [c_i64, c_i32, c_i64, c_i32, c_i32, c_i32, c_f32,
+                                                 c_void_p, c_size, c_void_p]),
     "bloom_bias_gelu_fwd": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_void_p]),
     "bloom_bias_gelu_bwd_workspace_size": (c_size, [c_i64, c_i64]),
     "bloom_bias_gelu_bwd": (ctypes.c_int, [c_void_p] * 6 + [c_size, c_i64, c_i64, c_void_p]),

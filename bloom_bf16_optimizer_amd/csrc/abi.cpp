@@ -55,7 +55,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int bloom_abi_version(void) { return 6; }
+int bloom_abi_version(void) { return 7; }
 
 const char* bloom_status_string(int status) {
   switch (status) {

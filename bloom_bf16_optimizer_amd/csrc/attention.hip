@@ -26,30 +26,16 @@
 // the host); P is rounded to bf16 for the P V product.
 #include <cmath>
 
-#include "device_common.h"
-#include "host_common.h"
+#include "attention_common.h"
 #include "launch_plan.h"
 
 namespace bloom {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
 constexpr int kAttnBlockM = 128;       // queries per workgroup (4 waves x 32)
 constexpr int kAttnBlockN = 64;        // keys per block
 constexpr int kAttnGroupThreads = 256; // one key stream: 4 waves, one per 32 queries
 constexpr int kAttnThreads = 2 * kAttnGroupThreads;  // two key streams over the same queries
-
-struct AttnSlopes {
-  float s[BLOOM_MAX_HEADS];  // slope_h * log2(e)
-};
-
-__device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
 // One key block of K or V in LDS: 64 rows of D bf16, row-major, unpadded,
 // written straight from global memory by global_load_lds_dwordx4 (each lane
@@ -72,24 +58,6 @@ struct AttnTile {
   __device__ static int swz_k(int r) { return (r / RPB) % CPR; }
   __device__ static int swz_v(int r) { return 4 * ((r / RPB) % (CPR / 4)); }
 };
-
-typedef __attribute__((address_space(3))) uint4 attn_lds_uint4;
-typedef unsigned int attn_u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) attn_u32x4 attn_lds_u32x4;
-typedef short attn_v4s __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) attn_v4s attn_lds_v4s;
-
-// One 16-byte-per-lane transfer from global memory (wave-uniform base plus
-// a 32-bit byte offset per lane) into LDS at m0 + lane*16 (cached: K and V
-// are re-read by every query block of the head).  m0 is written only here:
-// the compiler uses it for nothing else in this kernel (checked in the
-// generated code), so the clobber is only a precaution.
-__device__ __forceinline__ void attn_dma16(const void* sbase, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(m0)
-               : "memory", "m0");
-}
 
 // Requests key block [k0, k0+64) of K (SWZ_V false) or V into `tile`; this
 // wave (wq of the stream's four) moves chunks [64*(4x + wq), +64) for each

@@ -1,0 +1,531 @@
+// Fused causal attention with the ALiBi bias, backward, for gfx950.
+//
+// What is computed: the gradient of the attention of BLOOM's blocks (ALiBi
+// bias of page "BLOOM 176B 训练技术概览", section "架构微调"; the combined
+// scale + mask + softmax of "融合 CUDA 核" between Q K^T and V, run backward
+// in training) for an upstream gradient dO, from q, k, v and the forward's
+// log-sum-exp lse, without the L x L matrices:
+//   p_ij  = exp(scale*(q_i . k_j) - slope_h*(i - j) - lse_i)   (j <= i, else 0)
+//   dp_ij = dO_i . v_j,   D_i = sum_j p_ij dp_ij,   ds_ij = p_ij (dp_ij - D_i)
+//   dq_i  = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
+//   dv_j  = sum_i p_ij dO_i.
+//
+// Two kernels, each owning its outputs (no atomics, results independent of
+// scheduling):
+//  * dq: a workgroup of four waves takes 128 consecutive queries of one (b, h),
+//    a wave 32, and streams the key blocks (64 keys, K and V staged in LDS)
+//    up to its diagonal, twice.  Both passes form S^T = K Q^T and dP^T = V dO^T
+//    so that lane l owns query l%32 (its lse and D_i are one number each).
+//    The first pass sums D_i = sum_j p_ij dp_ij in FP32; the second forms dS
+//    and dQ^T += K^T dS^T with K^T read from the same LDS tile by the
+//    transposing ds_read_b64_tr_b16.  It also writes D_i for the second kernel.
+//    (The usual shortcut D_i = dO_i . o_i from the stored bf16 o carries that
+//    rounding, 2^-9 of sum_d |dO_id o_id|, into every ds_ij of the row at
+//    weight p_ij; with ALiBi's steep slopes p is often near 1 on the diagonal
+//    and the error reaches the outputs.)
+//  * dk/dv: a workgroup takes 128 consecutive keys, a wave 32, and streams the
+//    query blocks (64 queries, Q and dO staged in LDS, with their lse and D)
+//    from its diagonal to the end.  It forms S = Q K^T and dP = dO V^T so that
+//    lane l owns key l%32, then dV^T += dO^T P and dK^T += Q^T dS with dO^T and
+//    Q^T read transposed from the staged tiles.
+// Products use v_mfma_f32_32x32x16_bf16 with FP32 accumulation.  P enters
+// as bf16 (it is >= 0, so its rounding stays relative to the result).  dS
+// enters dQ and dK as two bf16 parts, hi = bf16(ds) and lo = bf16(ds - hi),
+// i.e. with about 16 significant bits: dq and dk are sums of terms of both
+// signs that can cancel to far below their size, where a single bf16
+// rounding of ds (2^-9 of each term) would show in the result.  The
+// exponentials are base 2 (scale, slopes and lse pre-multiplied by log2 e).
+#include <cmath>
+
+#include "attention_common.h"
+
+namespace bloom {
+namespace {
+
+constexpr int kBwdThreads = 256;  // four waves
+constexpr int kBwdRows = 64;      // rows of a staged tile (keys for dq, queries for dk/dv)
+constexpr int kBwdBlock = 128;    // queries (dq) or keys (dk/dv) per workgroup, 32 per wave
+constexpr float kLog2e = 1.4426950408889634f;
+
+// One staged tile: 64 rows of D bf16, row-major, written straight from global
+// memory by global_load_lds_dwordx4.  Chunk c (16 bytes) of row r sits at
+// c ^ swz(r).  The tiles are read two ways: one chunk per lane down 16
+// consecutive rows (an MFMA operand with the row index on the lanes), and by
+// the transposing read, two adjacent chunks (an even one and the next) of 4
+// consecutive rows per 16-lane group.  swz keeps both free of bank conflicts:
+// it takes 16 distinct values over 16 consecutive row groups (RPB rows share
+// 256 bytes), and within 4 consecutive rows its values differ above bit 0.
+template <int D>
+struct BwdTile {
+  static constexpr int CPR = D / 8;    // 16-byte chunks per row
+  static constexpr int RPB = 16 / CPR; // rows per 256 bytes
+  static constexpr int Q4 = CPR / 4;
+  static constexpr int CHUNKS = kBwdRows * CPR;
+  static constexpr int DMA = CHUNKS / kBwdThreads;  // transfers per lane per tile
+  static_assert(DMA >= 1 && CHUNKS % kBwdThreads == 0, "tile size");
+  __device__ static int swz(int r) {
+    const int x = r / RPB;
+    return 4 * (x % Q4) + (x / Q4) % 4;
+  }
+};
+
+// Requests rows [r0, r0+64) of a [seq, D] matrix (row index base + r) into
+// `tile`; wave w of the four moves chunks [64*(4x + w), +64) for each x.  Rows
+// past the end re-read row seq-1 (every use of them is masked).
+template <int D>
+__device__ __forceinline__ void bwd_request(const uint4* __restrict__ g, attn_lds_uint4* tile, int64_t base, int r0,
+                                           int seq, int w, int lane) {
+  using T = BwdTile<D>;
+  const uint4* gb = attn_uniform(g + (base + r0) * T::CPR);
+  const bool tail = r0 + kBwdRows > seq;  // wave-uniform
+#pragma unroll
+  for (int x = 0; x < T::DMA; ++x) {
+    const int first = (4 * x + w) * kWave;
+    const int slot = first + lane;
+    const int r = slot / T::CPR, pc = slot % T::CPR;
+    const int c = pc ^ T::swz(r);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(tile + first));
+    const int row = tail ? min(r, seq - 1 - r0) : r;
+    attn_dma16(gb, (uint32_t)(row * T::CPR + c) * 16u, m0);
+  }
+}
+
+// The A operand of an MFMA from a staged tile read transposed: lane L gets
+// column d = 32*dt + L%32 of rows row0 + 4*(L/32) + {0..3} and of the same
+// rows + 8, which is the k order of the P / dS fragments below.
+template <int D>
+__device__ __forceinline__ bf16x8_t bwd_read_tr(const char __attribute__((address_space(3)))* bytes, int row0, int dt,
+                                                int trow, int tg, int tc, int sw0, int sw8) {
+  const int cc = 4 * dt + 2 * tg + (tc >> 1);
+  const int off0 = (row0 + trow) * (2 * D) + 16 * (cc ^ sw0) + 8 * (tc & 1);
+  const int off8 = (row0 + trow + 8) * (2 * D) + 16 * (cc ^ sw8) + 8 * (tc & 1);
+  const attn_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((attn_lds_v4s*)(bytes + off0));
+  const attn_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((attn_lds_v4s*)(bytes + off8));
+  const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
+  return as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
+}
+
+// x as hi + lo, both bf16: hi = RNE(x), lo = RNE(x - hi) (x - hi is exact in FP32).
+struct Bf16Pair {
+  __bf16 hi, lo;
+};
+__device__ __forceinline__ Bf16Pair split_bf16(float x) {
+  const __bf16 hi = (__bf16)x;
+  return {hi, (__bf16)(x - (float)hi)};
+}
+
+// ---------------------------------------------------------------------------
+// dq kernel: one key block for one wave.  s, dp: rows = keys
+// k0 + 32*kt + 8*(i/4) + 4*half + i%4, column = this lane's query qi.
+// SUM: the first pass, which only adds p * dp into dsum; otherwise the
+// second, which forms dS with the row's D = delta and accumulates dQ^T.
+template <int D, bool DIAG, bool SUM>
+__device__ __forceinline__ void dq_block(f32x16_t (&acc)[D / 32], float& dsum, const attn_lds_uint4* __restrict__ kt_lds,
+                                         const attn_lds_uint4* __restrict__ vt_lds, const bf16x8_t (&qf)[D / 16],
+                                         const bf16x8_t (&df)[D / 16], float scale2, float slope2, float lse2,
+                                         float delta, int k0, int qi, int half, int col, int lane) {
+  using T = BwdTile<D>;
+  constexpr int KS = D / 16, DT = D / 32;
+  const f32x16_t zero = {};
+  f32x16_t s[2] = {zero, zero}, dp[2] = {zero, zero};
+  const int sw = T::swz(col);  // also the swizzle of row col + 32
+  const attn_lds_u32x4* k0r = reinterpret_cast<const attn_lds_u32x4*>(kt_lds) + col * T::CPR;
+  const attn_lds_u32x4* v0r = reinterpret_cast<const attn_lds_u32x4*>(vt_lds) + col * T::CPR;
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    const int c = (2 * kk + half) ^ sw;
+    s[0] = mfma32(__builtin_bit_cast(bf16x8_t, k0r[c]), qf[kk], s[0]);
+    s[1] = mfma32(__builtin_bit_cast(bf16x8_t, k0r[32 * T::CPR + c]), qf[kk], s[1]);
+    dp[0] = mfma32(__builtin_bit_cast(bf16x8_t, v0r[c]), df[kk], dp[0]);
+    dp[1] = mfma32(__builtin_bit_cast(bf16x8_t, v0r[32 * T::CPR + c]), df[kk], dp[1]);
+  }
+  // base-2 logit minus lse: s*scale2 + slope2*(key - qi) - lse2
+  const float cb = fmaf(slope2, (float)(k0 + 4 * half - qi), -lse2);
+  bf16x8_t dsh[4], dsl[4];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int off = 32 * kt + 8 * (i / 4) + (i % 4);  // key - k0 - 4*half
+      float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], scale2, fmaf(slope2, (float)off, cb)));
+      if (DIAG && k0 + 4 * half + off > qi) p = 0.f;
+      if (SUM) {
+        dsum = fmaf(p, dp[kt][i], dsum);
+      } else {
+        const Bf16Pair d2 = split_bf16(p * (dp[kt][i] - delta));
+        dsh[2 * kt + i / 8][i % 8] = d2.hi;
+        dsl[2 * kt + i / 8][i % 8] = d2.lo;
+      }
+    }
+  if (SUM) return;
+  // dQ^T += K^T dS^T over the 4 key steps of the block
+  const int tj = (lane & 15) >> 2, tc = lane & 3, tg = (lane >> 4) & 1;
+  const int trow = 4 * half + tj;
+  const int sw0 = T::swz(trow), sw8 = T::swz(trow + 8);  // the same for every step (rows + 16)
+  const char __attribute__((address_space(3)))* kbytes =
+      reinterpret_cast<const char __attribute__((address_space(3)))*>(kt_lds);
+#pragma unroll
+  for (int stp = 0; stp < 4; ++stp)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const bf16x8_t kT = bwd_read_tr<D>(kbytes, 16 * stp, dt, trow, tg, tc, sw0, sw8);
+      acc[dt] = mfma32(kT, dsh[stp], acc[dt]);
+      acc[dt] = mfma32(kT, dsl[stp], acc[dt]);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void attention_bwd_dq_kernel(
+    const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
+    const uint4* __restrict__ dout, const float* __restrict__ lse, uint2* __restrict__ dq,
+    float* __restrict__ delta_out, int seq, int heads, int qblocks, int bh_count,
+    float scale2, float scale, AttnSlopes slopes) {
+  constexpr int KS = D / 16, DT = D / 32, VPR = D / 8;
+  constexpr int CH = BwdTile<D>::CHUNKS;
+  __shared__ __attribute__((aligned(16))) uint4 tiles[2][2][CH];  // [stage][K, V]
+
+  const int t = threadIdx.x;
+  const int w = t / kWave, lane = t & (kWave - 1), half = lane >> 5, col = lane & 31;
+  // the longest workgroups (last query blocks) first
+  const int qb = qblocks - 1 - (int)(blockIdx.x / (unsigned)bh_count);
+  const int64_t bh = blockIdx.x % (unsigned)bh_count;
+  const int h = (int)(bh % heads);
+  const float slope2 = slopes.s[h];
+  const int64_t base = bh * (int64_t)seq;
+  const int q0 = qb * kBwdBlock + w * 32;
+  const int qi = q0 + col;
+  const bool qvalid = qi < seq;
+  const bool wave_live = q0 < seq;
+
+  // B operands: this lane's query row of q and dO (d = 16*kk + 8*half .. +8)
+  bf16x8_t qf[KS], df[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+    const int64_t idx = (base + qi) * VPR + 2 * kk + half;
+    qf[kk] = as_bf16x8(qvalid ? q[idx] : z4);
+    df[kk] = as_bf16x8(qvalid ? dout[idx] : z4);
+  }
+  const float lse2 = qvalid ? lse[base + qi] * kLog2e : 0.f;
+
+  f32x16_t acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+
+  const int wg_last_q = min(seq, (qb + 1) * kBwdBlock) - 1;
+  const int nkb = wg_last_q / kBwdRows + 1;  // key blocks nkb-1 .. 0, streamed once per pass
+  attn_lds_uint4* lt = (attn_lds_uint4*)&tiles[0][0][0];
+  auto tile = [&](int stage, int which) { return lt + (stage * 2 + which) * CH; };
+  float dsum = 0.f, delta = 0.f;
+  for (int pass = 0; pass < 2; ++pass) {
+    int kb = nkb - 1;
+    bwd_request<D>(k, tile(0, 0), base, kb * kBwdRows, seq, w, lane);
+    bwd_request<D>(v, tile(0, 1), base, kb * kBwdRows, seq, w, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int buf = 0; kb >= 0; --kb, buf ^= 1) {
+      const int k0 = kb * kBwdRows;
+      // the next block arrives while this one is used (the barrier that ended
+      // the previous iteration freed its buffer)
+      if (kb >= 1) {
+        bwd_request<D>(k, tile(buf ^ 1, 0), base, k0 - kBwdRows, seq, w, lane);
+        bwd_request<D>(v, tile(buf ^ 1, 1), base, k0 - kBwdRows, seq, w, lane);
+      }
+      if (wave_live && k0 <= q0 + 31) {
+        const bool diag = k0 + kBwdRows - 1 > q0;
+        if (pass == 0) {
+          if (diag)
+            dq_block<D, true, true>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta, k0,
+                                    qi, half, col, lane);
+          else
+            dq_block<D, false, true>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta, k0,
+                                     qi, half, col, lane);
+        } else {
+          if (diag)
+            dq_block<D, true, false>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta, k0,
+                                     qi, half, col, lane);
+          else
+            dq_block<D, false, false>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta,
+                                      k0, qi, half, col, lane);
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    if (pass == 0) {
+      // the two lane halves summed complementary keys of the same query
+      delta = dsum + __shfl_xor(dsum, 32, kWave);
+      if (qvalid && half == 0) delta_out[base + qi] = delta;
+    }
+  }
+  if (qvalid) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // d = 32*dt + 8*g + 4*half + 0..3
+        const uint32_t lo = pack2(acc[dt][4 * g] * scale, acc[dt][4 * g + 1] * scale);
+        const uint32_t hi = pack2(acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale);
+        dq[(base + qi) * (D / 4) + (32 * dt + 8 * g + 4 * half) / 4] = make_uint2(lo, hi);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dk/dv kernel: one 32-query tile (rows tr0 .. tr0+31 of the staged 64, global
+// queries qt0 ..) for one wave.  s, dp: rows = queries
+// qt0 + 8*(i/4) + 4*half + i%4, column = this lane's key kj.  MASK: some key
+// of the wave is after some query of the tile, or the tile runs past seq.
+template <int D, bool MASK>
+__device__ __forceinline__ void dkdv_tile(f32x16_t (&dkacc)[D / 32], f32x16_t (&dvacc)[D / 32],
+                                          const attn_lds_uint4* __restrict__ q_lds,
+                                          const attn_lds_uint4* __restrict__ do_lds, const float4* lse_lds,
+                                          const float4* delta_lds, const bf16x8_t (&kf)[D / 16],
+                                          const bf16x8_t (&vf)[D / 16], float scale2, float slope2, int kj, int tr0,
+                                          int qt0, int seq, int half, int col, int lane) {
+  using T = BwdTile<D>;
+  constexpr int KS = D / 16, DT = D / 32;
+  const f32x16_t zero = {};
+  f32x16_t s = zero, dp = zero;
+  const int sw = T::swz(tr0 + col);
+  const attn_lds_u32x4* qr = reinterpret_cast<const attn_lds_u32x4*>(q_lds) + (tr0 + col) * T::CPR;
+  const attn_lds_u32x4* dr = reinterpret_cast<const attn_lds_u32x4*>(do_lds) + (tr0 + col) * T::CPR;
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    const int c = (2 * kk + half) ^ sw;
+    s = mfma32(__builtin_bit_cast(bf16x8_t, qr[c]), kf[kk], s);
+    dp = mfma32(__builtin_bit_cast(bf16x8_t, dr[c]), vf[kk], dp);
+  }
+  // base-2 logit minus lse: s*scale2 + slope2*(kj - query) - lse2(query)
+  const float cb = slope2 * (float)(kj - qt0 - 4 * half);
+  bf16x8_t pf[2], dsh[2], dsl[2];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const float4 l4 = lse_lds[(tr0 + 8 * g + 4 * half) / 4];
+    const float4 d4 = delta_lds[(tr0 + 8 * g + 4 * half) / 4];
+    const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * g + r;
+      const int qoff = 8 * g + r;  // query - qt0 - 4*half
+      float p = __builtin_amdgcn_exp2f(fmaf(s[i], scale2, fmaf(-slope2, (float)qoff, cb) - lv[r]));
+      if (MASK) {
+        const int qq = qt0 + 4 * half + qoff;
+        if (kj > qq || qq >= seq) p = 0.f;
+      }
+      pf[i / 8][i % 8] = (__bf16)p;
+      const Bf16Pair d2 = split_bf16(p * (dp[i] - dv4[r]));
+      dsh[i / 8][i % 8] = d2.hi;
+      dsl[i / 8][i % 8] = d2.lo;
+    }
+  }
+  // dV^T += dO^T P and dK^T += Q^T dS over the tile's 2 query steps
+  const int tj = (lane & 15) >> 2, tc = lane & 3, tg = (lane >> 4) & 1;
+  const int trow = 4 * half + tj;
+  const int sw0 = T::swz(trow), sw8 = T::swz(trow + 8);  // unchanged by row offsets that are multiples of 16
+  const char __attribute__((address_space(3)))* qbytes =
+      reinterpret_cast<const char __attribute__((address_space(3)))*>(q_lds);
+  const char __attribute__((address_space(3)))* dbytes =
+      reinterpret_cast<const char __attribute__((address_space(3)))*>(do_lds);
+#pragma unroll
+  for (int stp = 0; stp < 2; ++stp)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      dvacc[dt] = mfma32(bwd_read_tr<D>(dbytes, tr0 + 16 * stp, dt, trow, tg, tc, sw0, sw8), pf[stp], dvacc[dt]);
+      const bf16x8_t qT = bwd_read_tr<D>(qbytes, tr0 + 16 * stp, dt, trow, tg, tc, sw0, sw8);
+      dkacc[dt] = mfma32(qT, dsh[stp], dkacc[dt]);
+      dkacc[dt] = mfma32(qT, dsl[stp], dkacc[dt]);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void attention_bwd_dkdv_kernel(
+    const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
+    const uint4* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    uint2* __restrict__ dk, uint2* __restrict__ dv, int seq, int heads, int bh_count, float scale2, float scale,
+    AttnSlopes slopes) {
+  constexpr int KS = D / 16, DT = D / 32, VPR = D / 8;
+  constexpr int CH = BwdTile<D>::CHUNKS;
+  __shared__ __attribute__((aligned(16))) uint4 tiles[2][2][CH];        // [stage][Q, dO]
+  __shared__ float4 rowv[2][2][kBwdRows / 4];                           // [stage][lse2, D] of the 64 queries
+
+  const int t = threadIdx.x;
+  const int w = t / kWave, lane = t & (kWave - 1), half = lane >> 5, col = lane & 31;
+  // the longest workgroups (first key blocks) first
+  const int kb = (int)(blockIdx.x / (unsigned)bh_count);
+  const int64_t bh = blockIdx.x % (unsigned)bh_count;
+  const int h = (int)(bh % heads);
+  const float slope2 = slopes.s[h];
+  const int64_t base = bh * (int64_t)seq;
+  const int kw0 = kb * kBwdBlock + w * 32;  // this wave's first key
+  const int kj = kw0 + col;
+  const bool kvalid = kj < seq;
+  const bool wave_live = kw0 < seq;
+
+  // B operands: this lane's key row of k and v (d = 16*kk + 8*half .. +8)
+  bf16x8_t kf[KS], vf[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+    const int64_t idx = (base + kj) * VPR + 2 * kk + half;
+    kf[kk] = as_bf16x8(kvalid ? k[idx] : z4);
+    vf[kk] = as_bf16x8(kvalid ? v[idx] : z4);
+  }
+  f32x16_t dkacc[DT], dvacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dkacc[dt][i] = dvacc[dt][i] = 0.f;
+
+  // Row values of a query block: lanes 0..15 of wave 0 move 4 lse values
+  // each, lanes 16..31 4 values of D (groups past seq re-read the last group;
+  // seq is a multiple of 8, so a group of 4 is wholly inside or outside).
+  auto row_load = [&](int r0) {
+    const int grp = r0 + 4 * (t & 15);
+    const int64_t at = base + min(grp, seq - 4);
+    return (t < 16) ? *reinterpret_cast<const float4*>(lse + at) : *reinterpret_cast<const float4*>(delta + at);
+  };
+  auto row_store = [&](int stage, float4 x) {
+    if (t < 16) x = make_float4(x.x * kLog2e, x.y * kLog2e, x.z * kLog2e, x.w * kLog2e);
+    rowv[stage][t >> 4][t & 15] = x;
+  };
+
+  const int nqb = (seq + kBwdRows - 1) / kBwdRows;
+  int qbi = (kb * kBwdBlock) / kBwdRows;  // the block holding this workgroup's first key
+  attn_lds_uint4* lt = (attn_lds_uint4*)&tiles[0][0][0];
+  auto tile = [&](int stage, int which) { return lt + (stage * 2 + which) * CH; };
+  bwd_request<D>(q, tile(0, 0), base, qbi * kBwdRows, seq, w, lane);
+  bwd_request<D>(dout, tile(0, 1), base, qbi * kBwdRows, seq, w, lane);
+  if (t < 32) row_store(0, row_load(qbi * kBwdRows));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int buf = 0; qbi < nqb; ++qbi, buf ^= 1) {
+    const int q0 = qbi * kBwdRows;
+    const bool next = qbi + 1 < nqb;
+    float4 rv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (next) {
+      bwd_request<D>(q, tile(buf ^ 1, 0), base, q0 + kBwdRows, seq, w, lane);
+      bwd_request<D>(dout, tile(buf ^ 1, 1), base, q0 + kBwdRows, seq, w, lane);
+      if (t < 32) rv = row_load(q0 + kBwdRows);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int qt0 = q0 + 32 * tt;
+      if (wave_live && qt0 < seq && kw0 <= qt0 + 31) {
+        if (kw0 + 31 > qt0 || qt0 + 32 > seq)
+          dkdv_tile<D, true>(dkacc, dvacc, tile(buf, 0), tile(buf, 1), rowv[buf][0], rowv[buf][1], kf, vf, scale2,
+                             slope2, kj, 32 * tt, qt0, seq, half, col, lane);
+        else
+          dkdv_tile<D, false>(dkacc, dvacc, tile(buf, 0), tile(buf, 1), rowv[buf][0], rowv[buf][1], kf, vf, scale2,
+                              slope2, kj, 32 * tt, qt0, seq, half, col, lane);
+      }
+    }
+    if (next && t < 32) row_store(buf ^ 1, rv);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  if (kvalid) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // d = 32*dt + 8*g + 4*half + 0..3
+        const int64_t at = (base + kj) * (D / 4) + (32 * dt + 8 * g + 4 * half) / 4;
+        dk[at] = make_uint2(pack2(dkacc[dt][4 * g] * scale, dkacc[dt][4 * g + 1] * scale),
+                            pack2(dkacc[dt][4 * g + 2] * scale, dkacc[dt][4 * g + 3] * scale));
+        dv[at] = make_uint2(pack2(dvacc[dt][4 * g], dvacc[dt][4 * g + 1]),
+                            pack2(dvacc[dt][4 * g + 2], dvacc[dt][4 * g + 3]));
+      }
+  }
+}
+
+size_t bwd_workspace(int64_t batch, int32_t heads, int64_t seq) {
+  return ((size_t)(batch * heads * seq) * sizeof(float) + 255) / 256 * 256;
+}
+
+template <int D>
+void launch_bwd(const bloom_bf16* q, const bloom_bf16* k, const bloom_bf16* v, const bloom_bf16* dout, const float* lse, bloom_bf16* dq, bloom_bf16* dk, bloom_bf16* dv,
+                float* delta, int64_t batch, int32_t heads, int64_t seq, float scale2, float scale,
+                const AttnSlopes& table, hipStream_t stream) {
+  const int bh_count = (int)(batch * heads);
+  const int blocks = (int)((seq + kBwdBlock - 1) / kBwdBlock);
+  const dim3 grid((unsigned)(bh_count * blocks));
+  const uint4* qv = reinterpret_cast<const uint4*>(q);
+  const uint4* kv = reinterpret_cast<const uint4*>(k);
+  const uint4* vv = reinterpret_cast<const uint4*>(v);
+  const uint4* dov = reinterpret_cast<const uint4*>(dout);
+  hipLaunchKernelGGL((attention_bwd_dq_kernel<D>), grid, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov, lse,
+                     reinterpret_cast<uint2*>(dq), delta, (int)seq, (int)heads, blocks, bh_count, scale2, scale,
+                     table);
+  hipLaunchKernelGGL((attention_bwd_dkdv_kernel<D>), grid, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov, lse,
+                     delta, reinterpret_cast<uint2*>(dk), reinterpret_cast<uint2*>(dv), (int)seq, (int)heads,
+                     bh_count, scale2, scale, table);
+}
+
+}  // namespace
+}  // namespace bloom
+
+using namespace bloom;
+
+extern "C" size_t bloom_alibi_attention_bwd_workspace_size(int64_t batch, int32_t heads, int64_t seq) {
+  if (batch < 0 || heads < 0 || heads > BLOOM_MAX_HEADS || seq < 0 || seq > BLOOM_MAX_SEQ) return 0;
+  if (batch * heads * seq == 0) return 256;
+  return bwd_workspace(batch, heads, seq);
+}
+
+extern "C" bloom_status bloom_alibi_attention_bwd(const bloom_bf16* q, const bloom_bf16* k, const bloom_bf16* v,
+                                                  const bloom_bf16* dout, const float* lse,
+                                                  bloom_bf16* dq, bloom_bf16* dk, bloom_bf16* dv, int64_t batch,
+                                                  int32_t heads, int64_t seq, int32_t head_dim,
+                                                  int32_t head_offset, int32_t total_heads, float scale,
+                                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  BLOOM_REQUIRE(batch >= 0 && heads >= 0, BLOOM_ERR_SHAPE, "batch and heads must be >= 0");
+  BLOOM_REQUIRE(heads <= BLOOM_MAX_HEADS, BLOOM_ERR_SHAPE, "heads = %d exceeds %d", heads, BLOOM_MAX_HEADS);
+  BLOOM_REQUIRE(seq >= 8 && seq <= BLOOM_MAX_SEQ && seq % 8 == 0, BLOOM_ERR_SHAPE,
+                "seq = %lld must be a multiple of 8 in [8, %d]", (long long)seq, BLOOM_MAX_SEQ);
+  BLOOM_REQUIRE(head_dim == 32 || head_dim == 64 || head_dim == 128, BLOOM_ERR_SHAPE,
+                "head_dim = %d must be 32, 64 or 128", head_dim);
+  BLOOM_REQUIRE(batch * heads * ((seq + kBwdBlock - 1) / kBwdBlock) <= 0x7fffffffLL, BLOOM_ERR_SHAPE,
+                "too many blocks");
+  BLOOM_REQUIRE(std::isfinite(scale) && scale >= 1e-30f, BLOOM_ERR_HPARAM, "scale = %g must be finite and >= 1e-30",
+                (double)scale);
+  BLOOM_REQUIRE(total_heads > 0 && head_offset >= 0 && (int64_t)head_offset + heads <= total_heads,
+                BLOOM_ERR_SHAPE, "heads [%d, %d) outside a %d-head model", head_offset, head_offset + heads,
+                total_heads);
+  if (batch == 0 || heads == 0) return BLOOM_OK;
+  BLOOM_REQUIRE_PTR(q);
+  BLOOM_REQUIRE_PTR(k);
+  BLOOM_REQUIRE_PTR(v);
+  BLOOM_REQUIRE_PTR(dout);
+  BLOOM_REQUIRE_PTR(lse);
+  BLOOM_REQUIRE_PTR(dq);
+  BLOOM_REQUIRE_PTR(dk);
+  BLOOM_REQUIRE_PTR(dv);
+  BLOOM_REQUIRE(workspace != nullptr, BLOOM_ERR_WORKSPACE, "workspace is NULL");
+  BLOOM_REQUIRE(aligned16(workspace), BLOOM_ERR_ALIGN, "workspace is not 16-byte aligned");
+  const size_t need = bwd_workspace(batch, heads, seq);
+  BLOOM_REQUIRE(workspace_bytes >= need, BLOOM_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                need);
+  float sl[BLOOM_MAX_HEADS];
+  if (bloom_status st = bloom_alibi_slopes(total_heads, head_offset, heads, sl)) return st;
+  AttnSlopes table;
+  const double log2e = 1.4426950408889634;
+  for (int hh = 0; hh < BLOOM_MAX_HEADS; ++hh) table.s[hh] = (hh < heads) ? (float)((double)sl[hh] * log2e) : 0.f;
+  const float scale2 = (float)((double)scale * log2e);
+  float* delta = static_cast<float*>(workspace);
+  switch (head_dim) {
+    case 32:
+      launch_bwd<32>(q, k, v, dout, lse, dq, dk, dv, delta, batch, heads, seq, scale2, scale, table, stream);
+      break;
+    case 64:
+      launch_bwd<64>(q, k, v, dout, lse, dq, dk, dv, delta, batch, heads, seq, scale2, scale, table, stream);
+      break;
+    default:
+      launch_bwd<128>(q, k, v, dout, lse, dq, dk, dv, delta, batch, heads, seq, scale2, scale, table, stream);
+      break;
+  }
+  return launch_status("bloom_alibi_attention_bwd");
+}

@@ -159,6 +159,27 @@ def bloom_alibi_attention_fwd(q, k, v, o, lse, head_offset: int, total_heads: in
         b, h, s, d, head_offset, total_heads, scale, _stream()))
 
 
+def bloom_alibi_attention_bwd_workspace_size(batch: int, heads: int, seq: int) -> int:
+    return _lib.load().bloom_alibi_attention_bwd_workspace_size(batch, heads, seq)
+
+
+def bloom_alibi_attention_bwd(q, k, v, dout, lse, dq, dk, dv, head_offset: int, total_heads: int, scale: float,
+                              workspace) -> None:
+    if q.dim() != 4:
+        raise ValueError("q must be [batch, heads, seq, head_dim]")
+    b, h, s, d = q.shape
+    for t, name in ((k, "k"), (v, "v"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _same(q, t, f"q/{name}")
+    if lse.numel() != b * h * s:
+        raise ValueError("lse must have batch*heads*seq elements")
+    wsb = workspace.numel() * workspace.element_size()
+    lib = _lib.load()
+    check("bloom_alibi_attention_bwd", lib.bloom_alibi_attention_bwd(
+        _ptr(q, BF16, "q"), _ptr(k, BF16, "k"), _ptr(v, BF16, "v"), _ptr(dout, BF16, "dout"),
+        _ptr(lse, F32, "lse"), _ptr(dq, BF16, "dq"), _ptr(dk, BF16, "dk"), _ptr(dv, BF16, "dv"),
+        b, h, s, d, head_offset, total_heads, scale, _ptr(workspace, workspace.dtype, "workspace"), wsb, _stream()))
+
+
 def bloom_bias_gelu_fwd(x, bias, y) -> None:
     rows, cols = _rows_cols(x)
     _same(x, y, "x/y")

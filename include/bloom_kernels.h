@@ -193,6 +193,36 @@ bloom_status bloom_alibi_attention_fwd(const bloom_bf16* q, const bloom_bf16* k,
                                        int64_t seq, int32_t head_dim, int32_t head_offset,
                                        int32_t total_heads, float scale, hipStream_t stream);
 
+/* Fused causal attention with the ALiBi bias, backward: the gradients of
+ * bloom_alibi_attention_fwd's o with respect to q, k and v for an upstream
+ * gradient dout, without the L x L matrices (same passages as the forward;
+ * training runs every fused kernel backward too):
+ *   p_ij  = exp(scale*(q_i . k_j) - slope_h*(i - j) - lse_i)  (j <= i, else 0)
+ *   dp_ij = dout_i . v_j,  D_i = sum_j p_ij dp_ij (FP32),
+ *   ds_ij = p_ij * (dp_ij - D_i)
+ *   dq_i  = scale * sum_j ds_ij k_j,  dk_j = scale * sum_i ds_ij q_i,
+ *   dv_j  = sum_i p_ij dout_i
+ * q, k, v, dout, dq, dk, dv [batch, heads, seq, head_dim] bf16 row-major;
+ * lse [batch, heads, seq] fp32 as written by the forward (natural log); the
+ * forward's o is not needed (D is summed from p and dp, not as dout . o).
+ * Shapes, slopes and scale as for bloom_alibi_attention_fwd.  p enters the
+ * dv product as bf16; ds enters the dq and dk products as two bf16 parts
+ * (about 16 significant bits, since those sums can cancel); products
+ * accumulate in FP32.
+ * Deterministic: each output element is written by one workgroup.  The
+ * caller-owned device workspace (16-byte aligned, at least
+ * bloom_alibi_attention_bwd_workspace_size bytes; its contents are not
+ * needed between calls) holds D.  dq, dk, dv must not overlap the inputs or
+ * each other.  BLOOM_ERR_WORKSPACE if the workspace is NULL or too small.
+ */
+size_t bloom_alibi_attention_bwd_workspace_size(int64_t batch, int32_t heads, int64_t seq);
+bloom_status bloom_alibi_attention_bwd(const bloom_bf16* q, const bloom_bf16* k, const bloom_bf16* v,
+                                       const bloom_bf16* dout, const float* lse,
+                                       bloom_bf16* dq, bloom_bf16* dk, bloom_bf16* dv, int64_t batch,
+                                       int32_t heads, int64_t seq, int32_t head_dim, int32_t head_offset,
+                                       int32_t total_heads, float scale, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * bias + GeLU forward.  [overview] "融合 CUDA 核" (bias + GeLU fusion); the
  * MLP's GeLU(XA) of [3d] 2.1.  tanh form (Hendrycks and Gimpel,

@@ -20,7 +20,7 @@ from dataclasses import dataclass, field
 S_LN_X, S_LN_GAMMA, S_LN_BETA, S_LN_DY = 1, 2, 3, 4
 S_LN_RES, S_LN_DRES = 5, 6  # residual-stream input and its gradient (fused LayerNorm + residual)
 S_SM_SCORES, S_SM_DPROBS = 10, 11
-S_ATT_Q, S_ATT_K, S_ATT_V = 12, 13, 14  # fused attention inputs
+S_ATT_Q, S_ATT_K, S_ATT_V, S_ATT_DO = 12, 13, 14, 15  # fused attention inputs and the output gradient
 S_GELU_X, S_GELU_BIAS, S_GELU_DY = 20, 21, 22
 S_OPT_PARAM, S_OPT_ACC, S_OPT_M, S_OPT_V = 30, 31, 32, 33
 S_OPT_GRAD0 = 100  # micro-batch k (1-based) uses stream S_OPT_GRAD0 + k

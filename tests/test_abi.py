@@ -37,7 +37,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for required in ["bloom_alibi_attention_fwd", "bloom_bf16_adamw_step_segments", "bloom_lr_warmup_cosine",
+    for required in ["bloom_alibi_attention_fwd", "bloom_alibi_attention_bwd", "bloom_bf16_grad_accumulate_many",
+                     "bloom_bf16_adamw_step_segments", "bloom_lr_warmup_cosine",
                      "bloom_layernorm_fwd", "bloom_layernorm_bwd", "bloom_layernorm_residual_fwd",
                      "bloom_layernorm_residual_bwd", "bloom_alibi_softmax_fwd",
                      "bloom_alibi_softmax_bwd", "bloom_bias_gelu_fwd", "bloom_bias_gelu_bwd",
@@ -52,7 +53,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.bloom_abi_version() == 6
+    assert lib.bloom_abi_version() == 7
     assert lib.bloom_status_string(0) == b"ok"
     assert lib.bloom_status_string(4) == b"workspace too small"
     assert lib.bloom_status_string(99) == b"unknown status"
@@ -230,3 +231,25 @@ def test_attention_validation(lib):
     assert f(p, p, p, None, p, 1, 4, 64, 128, 0, 4, 0.1, None) == NULL
     assert f(p, p, p, p + 8, p, 1, 4, 64, 128, 0, 4, 0.1, None) == ALIGN
     assert f(p, p, p, p, p, 0, 4, 64, 128, 0, 4, 0.1, None) == OK           # empty
+
+
+def test_attention_bwd_validation(lib):
+    p = FAKE
+    ws = lib.bloom_alibi_attention_bwd_workspace_size(1, 4, 64)
+    assert ws >= 4 * 4 * 64 and ws % 256 == 0
+    assert lib.bloom_alibi_attention_bwd_workspace_size(-1, 4, 64) == 0
+    assert lib.bloom_alibi_attention_bwd_workspace_size(1, 4, 1 << 30) == 0
+    f = lib.bloom_alibi_attention_bwd
+    ok = (1, 4, 64, 128, 0, 4, 0.1)
+    assert f(p, p, p, p, p, p, p, p, 1, 4, 100, 128, 0, 4, 0.1, p, ws, None) == SHAPE   # seq not a multiple of 8
+    assert f(p, p, p, p, p, p, p, p, 1, 4, 64, 96, 0, 4, 0.1, p, ws, None) == SHAPE    # head_dim
+    assert f(p, p, p, p, p, p, p, p, 1, 4, 64, 128, 2, 4, 0.1, p, ws, None) == SHAPE   # heads outside the model
+    assert f(p, p, p, p, p, p, p, p, 1, 4, 64, 128, 0, 4, float("inf"), p, ws, None) == HPARAM
+    assert f(p, p, p, p, p, p, p, p, 1, 4, 64, 128, 0, 4, 0.0, p, ws, None) == HPARAM
+    assert f(p, p, p, None, p, p, p, p, *ok, p, ws, None) == NULL                         # dout
+    assert f(p, p, p, p, p, p, None, p, *ok, p, ws, None) == NULL                         # dk
+    assert f(p, p, p, p, p + 4, p, p, p, *ok, p, ws, None) == ALIGN                       # lse
+    assert f(p, p, p, p, p, p, p, p, *ok, None, ws, None) == WORKSPACE
+    assert f(p, p, p, p, p, p, p, p, *ok, p, ws - 16, None) == WORKSPACE
+    assert f(p, p, p, p, p, p, p, p, *ok, p + 8, ws, None) == ALIGN
+    assert f(p, p, p, p, p, p, p, p, 0, 4, 64, 128, 0, 4, 0.1, None, 0, None) == OK    # empty: nothing enqueued
