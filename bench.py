@@ -71,6 +71,10 @@ def bytes_model(sh, n, mb, batch=GRAD_BUFFERS):
         "alibi_attention_fwd": b * h * s * sh["head_dim"] * 2 * 4 + b * h * s * 4,
         # ... and its MFMA work: q.k and p.v take 2*D flops each per causal (query, key <= query) pair
         "_attention_flops": 2 * 2 * b * h * (s * (s + 1) // 2) * sh["head_dim"],
+        # backward: q, k, v, dout read and dq, dk, dv written (bf16), lse read (fp32)
+        "alibi_attention_bwd": b * h * s * sh["head_dim"] * 2 * 7 + b * h * s * 4,
+        # ... five products per causal pair: q.k, dout.v, p^T.dout, ds.k, ds^T.q
+        "_attention_bwd_flops": 5 * 2 * b * h * (s * (s + 1) // 2) * sh["head_dim"],
         "alibi_softmax_fwd": live * 2 + full * 2,
         "alibi_softmax_bwd": live * 4 + full * 2,
         "bias_gelu_fwd": grows * gcols * 4 + gcols * 2,
@@ -236,6 +240,20 @@ def run_gpu(args):
         return lambda: ops.bloom_alibi_attention_fwd(q, k, v, o, lse, X.softmax.head_offset, X.softmax.total_heads,
                                                      scale)
 
+    def att_bwd_set(s):
+        q = fill((smb, smh, sms, hd), W.S_ATT_Q, 1.0, s=s)
+        k = fill((smb, smh, sms, hd), W.S_ATT_K, 1.0, s=s)
+        v = fill((smb, smh, sms, hd), W.S_ATT_V, 1.0, s=s)
+        do = fill((smb, smh, sms, hd), W.S_ATT_DO, 1.0, s=s)
+        o = torch.empty_like(q)
+        lse = torch.empty((smb, smh, sms), dtype=f32, device=dev)
+        ops.bloom_alibi_attention_fwd(q, k, v, o, lse, X.softmax.head_offset, X.softmax.total_heads, scale)
+        del o
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        ws = torch.empty(ops.bloom_alibi_attention_bwd_workspace_size(smb, smh, sms), dtype=torch.uint8, device=dev)
+        return lambda: ops.bloom_alibi_attention_bwd(q, k, v, do, lse, dq, dk, dv, X.softmax.head_offset,
+                                                     X.softmax.total_heads, scale, ws)
+
     L = W.LONG.softmax  # the 8192-token extrapolation shape, 28 heads
 
     def att_fwd_long_set(s):
@@ -251,7 +269,8 @@ def run_gpu(args):
         return lambda: ops.bloom_bf16_grad_accumulate(acc, grads[s], False)
 
     sweep_only = [("layernorm_residual_fwd", lnr_fwd_set, 4), ("layernorm_residual_bwd", lnr_bwd_set, 4),
-                  ("alibi_attention_fwd", att_fwd_set, 4), ("alibi_attention_fwd_8192", att_fwd_long_set, 2)]
+                  ("alibi_attention_fwd", att_fwd_set, 4), ("alibi_attention_fwd_8192", att_fwd_long_set, 2),
+                  ("alibi_attention_bwd", att_bwd_set, 4)]
     if batch > 1:
         sweep_only.append(("grad_accumulate", acc_one_set, GRAD_BUFFERS))
 
@@ -473,10 +492,11 @@ def main():
                       else "events around each launch in the timed steps"}
         if k in sweep:
             kernels[k]["in_step_ms"] = round(in_step[k], 4) if k in in_step else None
-    for att, fk in (("alibi_attention_fwd", "_attention_flops"), ("alibi_attention_fwd_8192", "_attention_flops_8192")):
+    for att, fk in (("alibi_attention_fwd", "_attention_flops"), ("alibi_attention_fwd_8192", "_attention_flops_8192"),
+                    ("alibi_attention_bwd", "_attention_bwd_flops")):
         if att not in kernels:
             continue
-        # causal: q.k and p.v each take 2*D flops for every (query, key <= query) pair
+        # causal: each D-wide product takes 2*D flops for every (query, key <= query) pair
         flops = bts[fk]
         tf = flops / (per[att] * 1e-3) / 1e12
         kernels[att].update({"flops": flops, "TFLOP/s": round(tf, 1),

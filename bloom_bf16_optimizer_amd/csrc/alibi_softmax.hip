@@ -182,6 +182,15 @@ bloom_status check_softmax(int64_t batch, int32_t heads, int64_t seq) {
 
 RowPlan plan_softmax(int64_t rows_total, int vecs) { return plan_rows_fwd(rows_total, vecs); }
 
+// With a wave per row (rows up to 4096 wide), the kernels reserve LDS they
+// never touch so that fewer workgroups share a compute unit: at most 6 in the
+// forward and 4 in the backward.  Fewer row streams in flight measured 3 %
+// and 2 % faster at [1, 28, 2048, 2048] than the 8 the registers allow.
+size_t cap_lds(const RowPlan& p, bool bwd) {
+  if (p.tpr != kWave) return 0;
+  return bwd ? 40 * 1024 : 24 * 1024;
+}
+
 }  // namespace
 }  // namespace bloom
 
@@ -213,7 +222,7 @@ extern "C" bloom_status bloom_alibi_softmax_fwd(const bloom_bf16* scores, bloom_
   const uint4* src = reinterpret_cast<const uint4*>(scores);
   uint4* dst = reinterpret_cast<uint4*>(probs);
 #define CALL(NV, MAXB)                                                                   \
-  hipLaunchKernelGGL((softmax_fwd_kernel<NV, MAXB>), dim3(p.grid), dim3(p.block), 0, stream, \
+  hipLaunchKernelGGL((softmax_fwd_kernel<NV, MAXB>), dim3(p.grid), dim3(p.block), cap_lds(p, false), stream, \
                      src, dst, rows_total, (int)seq, vecs, p.tpr, (int)heads, scale2, table)
   BLOOM_ROW_DISPATCH(p, CALL);
 #undef CALL
@@ -237,7 +246,7 @@ extern "C" bloom_status bloom_alibi_softmax_bwd(const bloom_bf16* probs, const b
   const uint4* ds = reinterpret_cast<const uint4*>(dprobs);
   uint4* dst = reinterpret_cast<uint4*>(dscores);
 #define CALL(NV, MAXB)                                                                   \
-  hipLaunchKernelGGL((softmax_bwd_kernel<NV, MAXB>), dim3(p.grid), dim3(p.block), 0, stream, \
+  hipLaunchKernelGGL((softmax_bwd_kernel<NV, MAXB>), dim3(p.grid), dim3(p.block), cap_lds(p, true), stream, \
                      ys, ds, dst, rows_total, (int)seq, vecs, p.tpr, scale)
   BLOOM_ROW_DISPATCH(p, CALL);
 #undef CALL

@@ -37,6 +37,10 @@ constexpr int kBwdStageRows = 2;                         // rows per backward st
 constexpr int kBwdStages = 4;                            // stages per wave
 constexpr int kBwdRowsPerWave = kBwdStageRows * kBwdStages;
 constexpr int kBwdRows = 4 * kBwdRowsPerWave;            // rows per workgroup strip (one dbias partial row)
+// The backward reserves LDS it never touches so that at most two workgroups
+// (eight waves) share a compute unit: 4 % faster at [2048, 14336] than the
+// five its registers allow.
+constexpr size_t kBwdCapLds = 48 * 1024;
 
 struct GeluConsts {
   float a;     // -2k log2(e)
@@ -254,7 +258,7 @@ extern "C" bloom_status bloom_bias_gelu_bwd(const bloom_bf16* dy, const bloom_bf
   BLOOM_REQUIRE(workspace_bytes >= need, BLOOM_ERR_WORKSPACE,
                 "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   float* partial = static_cast<float*>(workspace);
-  hipLaunchKernelGGL(gelu_bwd_kernel, grid, dim3(4 * kWave), 0, stream,
+  hipLaunchKernelGGL(gelu_bwd_kernel, grid, dim3(4 * kWave), kBwdCapLds, stream,
                      reinterpret_cast<const uint4*>(dy), reinterpret_cast<const uint4*>(x),
                      reinterpret_cast<const uint4*>(bias), reinterpret_cast<uint4*>(dx), partial,
                      rows, vecs, gelu_consts());
