@@ -7,16 +7,17 @@ data already resident in HBM:
   ALiBi causal softmax fwd+bwd [1, 28, 2048, 2048] bf16 (heads 0..27 of 112)
   bias + GeLU fwd + bwd        [2048, 14336] bf16
   FP32 gradient accumulation   32 micro-batches of a 3.67e9-element bf16 gradient,
-                               8 resident micro-batch gradients added per pass
+                               16 resident micro-batch gradients added per pass
   BF16Optimizer step           global norm, clip 1.0, AdamW, bf16 parameter copy
 
 Each kernel reads inputs that were last touched a whole step earlier (the
 accumulation streams ~1.2 TB per step in between), so no kernel is served by
 the 256 MB Infinity Cache from the previous one.  The 32 micro-batch gradients
-cycle through GRAD_BUFFERS distinct 7.34 GB buffers (all 32 would need 235 GB).
-By default each accumulation pass adds `--accum-batch` (8) of them to the FP32
-accumulator in micro-batch order (4 passes of 24 B per element instead of 32 of
-10 B, bit-identical); `--accum-batch 1` times one pass per micro-batch.
+cycle through 16 distinct 7.34 GB buffers (117 GB; all 32 would need 235 GB).
+By default each accumulation pass adds `--accum-batch` (16) of them to the FP32
+accumulator in micro-batch order: 2 passes of 36 and 40 B per element instead of
+32 passes of 10 B, bit-identical; `--accum-batch 8` takes 4 passes (92 B per
+element) and `--accum-batch 1` one pass per micro-batch.
 
 Prints one JSON line.  `value` is the whole step's algorithmic HBM throughput
 (sum of each kernel's algorithmic bytes / step time, GB/s); per-kernel
@@ -45,7 +46,8 @@ if ROOT not in sys.path:
 METRIC = "achieved HBM GB/s (% of peak) per fused kernel; AdamW step ms @3.67B shard"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
-GRAD_BUFFERS = 8
+GRAD_BUFFERS = 16      # resident gradient buffers (at least --accum-batch of them)
+MAX_ACCUM_BATCH = 16   # the library limit on micro-batches per pass
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
 
@@ -138,6 +140,7 @@ def run_gpu(args):
     n = O.opt.n if args.n is None else args.n
     mb = O.opt.microbatches
     batch = args.accum_batch
+    nbuf = max(GRAD_BUFFERS, batch)
     rows, hid = X.ln.rows, X.ln.hidden
     smb, smh, sms = X.softmax.batch, X.softmax.heads, X.softmax.seq
     grows, gcols = X.gelu.rows, X.gelu.cols
@@ -272,15 +275,15 @@ def run_gpu(args):
                   ("alibi_attention_fwd", att_fwd_set, 4), ("alibi_attention_fwd_8192", att_fwd_long_set, 2),
                   ("alibi_attention_bwd", att_bwd_set, 4)]
     if batch > 1:
-        sweep_only.append(("grad_accumulate", acc_one_set, GRAD_BUFFERS))
+        sweep_only.append(("grad_accumulate", acc_one_set, nbuf))
 
-    log(f"bench: allocating the shard workload (n = {n:,}, {GRAD_BUFFERS} gradient buffers)")
+    log(f"bench: allocating the shard workload (n = {n:,}, {nbuf} gradient buffers)")
     master = fill((n,), W.S_OPT_PARAM, W.PARAM_SIGMA, dtype=f32)
     exp_avg = torch.zeros(n, dtype=f32, device=dev)
     exp_avg_sq = torch.zeros(n, dtype=f32, device=dev)
     acc = torch.empty(n, dtype=f32, device=dev)
     param = torch.empty(n, dtype=bf, device=dev)
-    grads = [fill((n,), W.S_OPT_GRAD0 + 1 + k, W.GRAD_SIGMA) for k in range(GRAD_BUFFERS)]
+    grads = [fill((n,), W.S_OPT_GRAD0 + 1 + k, W.GRAD_SIGMA) for k in range(nbuf)]
     norm = torch.empty(1, dtype=f32, device=dev)
     opt_ws = torch.empty(ops.bloom_bf16_adamw_workspace_size(n), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
@@ -309,7 +312,7 @@ def run_gpu(args):
             timed(name, fn, record)
         if batch == 1:
             for k in range(mb):
-                g = grads[k % GRAD_BUFFERS]
+                g = grads[k % nbuf]
                 if k == mb - 1:   # the last micro-batch also writes the norm's partial sums
                     timed("grad_accumulate_last", lambda g=g, k=k: ops.bloom_bf16_grad_accumulate_sumsq(
                         acc, g, k == 0, opt_ws), record)
@@ -318,7 +321,7 @@ def run_gpu(args):
                     timed(name, lambda g=g, k=k: ops.bloom_bf16_grad_accumulate(acc, g, k == 0), record)
         else:
             for k0 in range(0, mb, batch):
-                group = [grads[(k0 + j) % GRAD_BUFFERS] for j in range(batch)]
+                group = [grads[(k0 + j) % nbuf] for j in range(batch)]
                 last = k0 + batch == mb    # the last pass also writes the norm's partial sums
                 name = ("grad_accumulate_many_first" if k0 == 0 else
                         "grad_accumulate_many_last" if last else "grad_accumulate_many")
@@ -345,7 +348,8 @@ def run_gpu(args):
     in_step = {}
     for k in names:
         ts = [a.elapsed_time(b) for a, b in ev[k]]
-        in_step[k] = sum(ts) / len(ts)
+        if ts:   # with two accumulation passes there is no middle one
+            in_step[k] = sum(ts) / len(ts)
     log(f"bench: {ms_step:.2f} ms/step; grad norm {norm.item():.4f}")
 
     # Per-kernel sweep of the fused kernels: R back-to-back launches rotating
@@ -460,9 +464,9 @@ def main():
     ap.add_argument("--accum-batch", type=int, default=GRAD_BUFFERS,
                     help="resident micro-batch gradients added per accumulation pass (1 = one pass each)")
     args = ap.parse_args()
-    if not (1 <= args.accum_batch <= GRAD_BUFFERS) or (args.accum_batch > 1 and 32 % (2 * args.accum_batch)):
+    if not (1 <= args.accum_batch <= MAX_ACCUM_BATCH) or (args.accum_batch > 1 and 32 % (2 * args.accum_batch)):
         print(f"--accum-batch must be 1 or divide the 32 micro-batches into at least two passes of at most "
-              f"{GRAD_BUFFERS}", file=sys.stderr)
+              f"{MAX_ACCUM_BATCH}", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the hot path runs on a single MI355X at one GPU's shard shape, "
@@ -502,9 +506,14 @@ def main():
         kernels[att].update({"flops": flops, "TFLOP/s": round(tf, 1),
                              "frac_of_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                              "bound": "mfma (bf16 dense, 2500 TFLOP/s)"})
-    dom = "grad_accumulate" if batch == 1 else "grad_accumulate_many"
-    dom_label = ("grad_accumulate (micro-batches 2-31)" if batch == 1 else
-                 f"grad_accumulate_many ({batch} micro-batches per pass, passes 2-{mb // batch - 1})")
+    if batch == 1:
+        dom, dom_label = "grad_accumulate", "grad_accumulate (micro-batches 2-31)"
+    elif mb // batch > 2:
+        dom = "grad_accumulate_many"
+        dom_label = f"grad_accumulate_many ({batch} micro-batches per pass, passes 2-{mb // batch - 1})"
+    else:   # two passes: the second, which also writes the norm's partial sums
+        dom = "grad_accumulate_many_last"
+        dom_label = f"grad_accumulate_many ({batch} micro-batches per pass, pass 2 of 2, with the norm partials)"
     dom_gbs = bts[dom] / (per[dom] * 1e-3) / 1e9
     traffic = measured_traffic(dom)
     result = {
@@ -524,7 +533,7 @@ def main():
                                "fwd+bwd [1,28,2048,2048] (heads 0-27 of 112); bias-gelu fwd+bwd [2048,14336]; "
                                f"bf16-optimizer over a {n}-element shard with {mb} fp32-accumulated micro-batch "
                                "gradients, global-norm clip 1.0, adamw, rne bf16 copy",
-                   "optimizer_elements": n, "microbatches": mb, "grad_buffers": GRAD_BUFFERS,
+                   "optimizer_elements": n, "microbatches": mb, "grad_buffers": max(GRAD_BUFFERS, batch),
                    "microbatches_per_accumulation_pass": batch,
                    "storage": "bf16 activations and gradients, fp32 master/moments/accumulator"},
         "adamw_step_ms": round(per["adamw_step"], 3),

@@ -367,11 +367,19 @@ bloom_status launch_accumulate_many(float* acc, const GradPtrs& gp, int count, i
     case 5: launch_accumulate_many_k<5>(acc, gp, n, first, partial, stream); break;
     case 6: launch_accumulate_many_k<6>(acc, gp, n, first, partial, stream); break;
     case 7: launch_accumulate_many_k<7>(acc, gp, n, first, partial, stream); break;
-    default: launch_accumulate_many_k<8>(acc, gp, n, first, partial, stream); break;
+    case 8: launch_accumulate_many_k<8>(acc, gp, n, first, partial, stream); break;
+    case 9: launch_accumulate_many_k<9>(acc, gp, n, first, partial, stream); break;
+    case 10: launch_accumulate_many_k<10>(acc, gp, n, first, partial, stream); break;
+    case 11: launch_accumulate_many_k<11>(acc, gp, n, first, partial, stream); break;
+    case 12: launch_accumulate_many_k<12>(acc, gp, n, first, partial, stream); break;
+    case 13: launch_accumulate_many_k<13>(acc, gp, n, first, partial, stream); break;
+    case 14: launch_accumulate_many_k<14>(acc, gp, n, first, partial, stream); break;
+    case 15: launch_accumulate_many_k<15>(acc, gp, n, first, partial, stream); break;
+    default: launch_accumulate_many_k<16>(acc, gp, n, first, partial, stream); break;
   }
   return launch_status("bloom_bf16_grad_accumulate_many");
 }
-static_assert(BLOOM_MAX_ACCUM_BATCH == 8, "launch_accumulate_many covers 1..8 micro-batches");
+static_assert(BLOOM_MAX_ACCUM_BATCH == 16, "launch_accumulate_many covers 1..16 micro-batches");
 
 // Largest n: quad_blocks(n) must fit a 32-bit grid.
 constexpr int64_t kMaxElems = (int64_t)0x7ffffff0 * kBlockElems;

@@ -68,7 +68,7 @@ const char* bloom_last_error(void);
 #define BLOOM_MAX_HIDDEN 65536
 #define BLOOM_MAX_SEQ 16384
 #define BLOOM_MAX_HEADS 256
-#define BLOOM_MAX_ACCUM_BATCH 8
+#define BLOOM_MAX_ACCUM_BATCH 16
 
 /* ---------------------------------------------------------------------------
  * LayerNorm forward.  [overview] "融合 CUDA 核" (the fused LayerNorm kernel)

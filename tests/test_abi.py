@@ -172,9 +172,9 @@ def test_optimizer_validation(lib):
     assert acc(p, None, 10, 1, None) == NULL
     assert acc(p, p, 0, 0, None) == OK
     many = lib.bloom_bf16_grad_accumulate_many
-    ptrs = (ctypes.c_void_p * 9)(*([p] * 9))
+    ptrs = (ctypes.c_void_p * 17)(*([p] * 17))
     assert many(p, ptrs, 0, 1000, 1, None, 0, None) == SHAPE                # no micro-batch
-    assert many(p, ptrs, 9, 1000, 1, None, 0, None) == SHAPE                # more than BLOOM_MAX_ACCUM_BATCH
+    assert many(p, ptrs, 17, 1000, 1, None, 0, None) == SHAPE               # more than BLOOM_MAX_ACCUM_BATCH
     assert many(p, None, 2, 1000, 1, None, 0, None) == NULL
     assert many(p, (ctypes.c_void_p * 2)(p, None), 2, 1000, 1, None, 0, None) == NULL
     assert many(p, (ctypes.c_void_p * 2)(p, p + 8), 2, 1000, 1, None, 0, None) == ALIGN

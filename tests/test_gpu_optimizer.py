@@ -136,7 +136,7 @@ def test_fused_norm_partials_match_standalone(n, mb):
 
 
 @pytest.mark.parametrize("n,mb,batch", [(1_000_003, 11, 4), (4099, 8, 8), (7, 3, 2), (100_000, 32, 8), (1, 1, 1),
-                                        (3_000_000, 5, 3)])
+                                        (3_000_000, 5, 3), (100_003, 32, 16), (4099, 23, 11), (1_000_001, 16, 16)])
 def test_accumulate_many_bit_exact(n, mb, batch):
     """Several micro-batches per pass (groups of `batch`, the last possibly
     shorter): bit-identical to one pass per micro-batch and to the oracle's
