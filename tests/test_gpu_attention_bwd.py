@@ -58,10 +58,12 @@ def _oracle_lse(q, k, v, head_offset, total_heads, scale):
 
 
 # seq not a multiple of the 128-row workgroup blocks or the 64-row tiles;
-# head_offset inside a larger model; every head dimension
+# head_offset inside a larger model; every head dimension; several 128-row
+# blocks per head with a short last one (2, 4, 1000).
 @pytest.mark.parametrize("b,h,s,d,off,tot", [(1, 1, 8, 32, 0, 1), (2, 3, 24, 64, 5, 12), (1, 2, 136, 128, 0, 112),
                                             (1, 2, 200, 64, 100, 112), (3, 1, 72, 32, 3, 6), (1, 1, 264, 128, 0, 16),
-                                            (1, 4, 200, 64, 8, 112), (2, 2, 392, 128, 0, 2)])
+                                            (1, 4, 200, 64, 8, 112), (2, 2, 392, 128, 0, 2),
+                                            (2, 4, 1000, 64, 4, 16)])
 def test_attention_bwd_ragged(b, h, s, d, off, tot):
     require_gpu()
     q, k, v, do = _inputs(51, b, h, s, d)
