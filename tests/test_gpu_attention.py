@@ -66,6 +66,17 @@ def test_attention_long_context_sampled():
     _check("long 8192", q, k, v, s.head_offset, s.total_heads, s.scale, rows)
 
 
+@pytest.mark.timeout(900)
+def test_attention_max_seq_16384_sampled():
+    """The compiled sequence limit (BLOOM_MAX_SEQ = 16384): [1, 2, 16384, 128],
+    heads 0..1 of 112, sampled rows."""
+    require_gpu()
+    seq = 16384
+    q, k, v = _inputs(33, 1, 2, seq, 128)
+    rows = sample_rows(seq, 24, 33, must=(0, 8191, 8192, seq - 1))
+    _check("max seq 16384", q, k, v, 0, 112, float(np.float32(1.0 / np.sqrt(128.0))), rows)
+
+
 # seq not a multiple of the 128-query or 64-key blocks; head_offset inside a
 # larger model; every head dimension.  (1,4,200,64) and (2,2,392,128) have an
 # even number of query blocks and (b, h) pairs a multiple of 4, so they take

@@ -107,6 +107,24 @@ def test_attention_fwd_then_bwd_long_context_sampled():
     _check("long 8192", got, q, k, v, do, sm.head_offset, sm.total_heads, sm.scale, qrows=rows, krows=rows)
 
 
+@pytest.mark.timeout(900)
+def test_attention_fwd_then_bwd_max_seq_16384_sampled():
+    """The compiled sequence limit (BLOOM_MAX_SEQ = 16384), one head, the GPU
+    forward's lse feeding the backward: sampled query and key rows."""
+    require_gpu()
+    seq, heads, d = 16384, 1, 128
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    q, k, v, do = _inputs(34, 1, heads, seq, d)
+    tq, tk, tv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    to = torch.empty_like(tq)
+    tl = torch.empty((1, heads, seq), dtype=torch.float32, device="cuda")
+    ops.bloom_alibi_attention_fwd(tq, tk, tv, to, tl, 0, 112, scale)
+    torch.cuda.synchronize()
+    got = _bwd_gpu(q, k, v, do, tl.cpu().numpy(), 0, 112, scale)
+    rows = sample_rows(seq, 12, 34, must=(0, 8191, 8192, seq - 1))
+    _check("max seq 16384", got, q, k, v, do, 0, 112, scale, qrows=rows, krows=rows)
+
+
 def test_attention_bwd_chained_and_deterministic():
     require_gpu()
     b, h, s, d = 1, 4, 392, 128

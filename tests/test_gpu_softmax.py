@@ -144,6 +144,41 @@ def test_softmax_long_context_8192_sampled():
     assert np.all(got[j > i[:, None]] == 0)
 
 
+@pytest.mark.timeout(900)
+def test_softmax_max_seq_16384_sampled():
+    """Rows at the compiled sequence limit (BLOOM_MAX_SEQ = 16384): [1, 2, 16384,
+    16384], heads 0..1 of 112, 1.07 GB per tensor; forward and backward on
+    sampled rows.  The backward takes the forward's probabilities as y (both
+    sides see the same bits; the forward is checked on its own above it)."""
+    require_gpu()
+    b, h, seq, off, total = 1, 2, 16384, 0, 112
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    ts = torch.empty(b, h, seq, seq, dtype=torch.bfloat16, device="cuda")
+    sdev.fill_(ts, 31, W.S_SM_SCORES, W.ACT_SIGMA)
+    probs = _fwd_gpu(ts, off, total, scale)
+    rows_total = b * h * seq
+    sel = sample_rows(rows_total, 96, 31, must=(0, 1, 8191, 8192, seq - 1, seq, rows_total - 1))
+    tsel = torch.from_numpy(sel).cuda()
+    scores_rows = host_bf16(ts.view(-1, seq)[tsel])
+    del ts
+    slopes = oal.alibi_slopes_f32(total, off, h)
+    i = sel % seq
+    hh = (sel // seq) % h
+    yf = oal.softmax_fwd_f64(to_f64(scores_rows), i, slopes.astype(np.float64)[hh], scale)
+    got = host_bf16(probs.view(-1, seq)[tsel])
+    check_bf16("max-seq fwd (sampled rows)", got, round_to_bf16(yf), exact=yf)
+    j = np.arange(seq)[None, :]
+    assert np.all(got[j > i[:, None]] == 0)
+    tdy = torch.empty_like(probs)
+    sdev.fill_(tdy, 31, W.S_SM_DPROBS, W.ACT_SIGMA)
+    ds = _bwd_gpu(probs, tdy, scale)
+    dy_rows = host_bf16(tdy.view(-1, seq)[tsel])
+    dsf, terms = oal.softmax_bwd_f64(to_f64(got), to_f64(dy_rows), i, scale)
+    gds = host_bf16(ds.view(-1, seq)[tsel])
+    check_bf16("max-seq bwd (sampled rows)", gds, round_to_bf16(dsf), exact=dsf, terms=terms)
+    assert np.all(gds[j > i[:, None]] == 0)
+
+
 @pytest.mark.parametrize("b,h,s,off,total", [(1, 1, 8, 0, 1), (2, 3, 24, 1, 5), (1, 2, 136, 0, 2),
                                              (1, 2, 4104, 3, 12), (1, 1, 8200, 0, 1), (3, 4, 64, 60, 64),
                                              (1, 2, 520, 0, 112)])
