@@ -83,7 +83,7 @@ def test_attention_max_seq_16384_sampled():
 # the XCD-split workgroup order with a ragged last block.
 @pytest.mark.parametrize("b,h,s,d,off,tot", [(1, 1, 8, 32, 0, 1), (2, 3, 24, 64, 5, 12), (1, 2, 136, 128, 0, 112),
                                             (1, 2, 200, 64, 100, 112), (3, 1, 72, 32, 3, 6), (1, 1, 264, 128, 0, 16),
-                                            (1, 4, 200, 64, 8, 112), (2, 2, 392, 128, 0, 2)])
+                                            (1, 4, 200, 64, 8, 112), (2, 2, 392, 128, 0, 2), (1, 256, 24, 32, 0, 256)])
 def test_attention_ragged(b, h, s, d, off, tot):
     require_gpu()
     q, k, v = _inputs(41, b, h, s, d)

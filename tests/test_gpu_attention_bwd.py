@@ -63,7 +63,7 @@ def _oracle_lse(q, k, v, head_offset, total_heads, scale):
 @pytest.mark.parametrize("b,h,s,d,off,tot", [(1, 1, 8, 32, 0, 1), (2, 3, 24, 64, 5, 12), (1, 2, 136, 128, 0, 112),
                                             (1, 2, 200, 64, 100, 112), (3, 1, 72, 32, 3, 6), (1, 1, 264, 128, 0, 16),
                                             (1, 4, 200, 64, 8, 112), (2, 2, 392, 128, 0, 2),
-                                            (2, 4, 1000, 64, 4, 16)])
+                                            (2, 4, 1000, 64, 4, 16), (1, 256, 24, 32, 0, 256)])
 def test_attention_bwd_ragged(b, h, s, d, off, tot):
     require_gpu()
     q, k, v, do = _inputs(51, b, h, s, d)

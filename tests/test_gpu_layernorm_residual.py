@@ -84,7 +84,8 @@ def test_layernorm_residual_workloads_full(wl):
 # vectors per thread); (7, 16384): a 16-wave team whose ring + dres slot does
 # not fit in LDS, so the generic backward; (5, 4104), (3, 1000): generic
 # block and wave teams.
-@pytest.mark.parametrize("rows,hidden", [(600, 8192), (777, 5120), (7, 16384), (5, 4104), (3, 1000), (1, 8)])
+@pytest.mark.parametrize("rows,hidden", [(600, 8192), (777, 5120), (7, 16384), (5, 4104), (3, 1000), (1, 8),
+                                         (2, 65536)])
 def test_layernorm_residual_ragged(rows, hidden):
     require_gpu()
     _check(f"ragged {rows}x{hidden}", *_inputs(21, rows, hidden))

@@ -181,7 +181,7 @@ def test_softmax_max_seq_16384_sampled():
 
 @pytest.mark.parametrize("b,h,s,off,total", [(1, 1, 8, 0, 1), (2, 3, 24, 1, 5), (1, 2, 136, 0, 2),
                                              (1, 2, 4104, 3, 12), (1, 1, 8200, 0, 1), (3, 4, 64, 60, 64),
-                                             (1, 2, 520, 0, 112)])
+                                             (1, 2, 520, 0, 112), (1, 256, 24, 0, 256)])
 def test_softmax_ragged_shapes(b, h, s, off, total):
     require_gpu()
     scores = _scores_host(21, b, h, s)
