@@ -44,12 +44,13 @@ constexpr int64_t kBlockElems = 4 * kBlock;
 constexpr int kStage2Blocks = 2048;      // second reduction level (8 sums per finalize thread)
 
 // Occupancy cap for the passes with many concurrent streams (the multi
-// micro-batch accumulation reads 9 arrays, AdamW reads 4 and writes 4): each
-// workgroup reserves 31 KB of LDS it never touches, so at most 5 workgroups
-// (20 waves) share a CU.  Fewer requests in flight measured 1 % (accumulation
-// of 8) and 4 % (AdamW) faster than 8 workgroups per CU at 3.67e9 elements;
-// the one-gradient accumulation and the sum of squares measured slower with
-// the cap and launch without it.
+// micro-batch accumulation reads up to 17 arrays, AdamW reads 4 and writes 4):
+// each workgroup reserves 31 KB of LDS it never touches, so at most 5
+// workgroups (20 waves) share a CU.  Fewer requests in flight measured 1 %
+// (accumulation of 8) and 4 % (AdamW) faster than 8 workgroups per CU at
+// 3.67e9 elements, and 3 to 6 per CU within 0.3 % of each other for 8, 12 and
+// 16 gradients; the one-gradient accumulation and the sum of squares measured
+// slower with the cap and launch without it.
 constexpr size_t kCapLds = 31 * 1024;
 
 // Workgroups of a flat pass over n elements, rounded up to a multiple of 8 so
