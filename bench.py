@@ -92,6 +92,20 @@ def bytes_model(sh, n, mb, batch=GRAD_BUFFERS):
     }
 
 
+def long_context_model(ln_rows, hidden, batch, heads, seq, head_dim):
+    """Algorithmic bytes (and the attention's FLOP) of the 8192-token extrapolation rows."""
+    live = batch * heads * seq * (seq + 1) // 2
+    rows = batch * heads * seq
+    return {
+        # the embedding LayerNorm forward at the extrapolation length
+        "layernorm_fwd_8192": ln_rows * hidden * 4 + hidden * 4 + ln_rows * 8,
+        # causal softmax forward: the causal half read, the full rows written
+        "alibi_softmax_fwd_8192": live * 2 + batch * heads * seq * seq * 2,
+        "alibi_attention_fwd_8192": rows * head_dim * 2 * 4 + rows * 4,
+        "_attention_flops_8192": 2 * 2 * live * head_dim,
+    }
+
+
 def source_digest(*paths):
     h = hashlib.sha256()
     for p in paths:
@@ -267,13 +281,29 @@ def run_gpu(args):
         lse = torch.empty((L.batch, L.heads, L.seq), dtype=f32, device=dev)
         return lambda: ops.bloom_alibi_attention_fwd(q, k, v, o, lse, L.head_offset, L.total_heads, L.scale)
 
+    LW = W.LONG  # the 8192-token extrapolation: embedding LayerNorm and causal softmax forward
+
+    def ln_fwd_long_set(s):
+        x = fill((LW.ln.rows, LW.ln.hidden), W.S_LN_X, 1.0, s=s)
+        y = torch.empty_like(x)
+        m = torch.empty(LW.ln.rows, dtype=f32, device=dev)
+        r = torch.empty_like(m)
+        return lambda: ops.bloom_layernorm_fwd(x, ln_g, ln_b, y, m, r, W.LN_EPS)
+
+    def sm_fwd_long_set(s):
+        ls = LW.softmax
+        sc = fill((ls.batch, ls.heads, ls.seq, ls.seq), W.S_SM_SCORES, 1.0, s=s)   # 3.76 GB
+        p = torch.empty_like(sc)
+        return lambda: ops.bloom_alibi_softmax_fwd(sc, p, ls.head_offset, ls.total_heads, ls.scale)
+
     def acc_one_set(s):
         # one micro-batch per pass (a later micro-batch), over the resident gradient buffers
         return lambda: ops.bloom_bf16_grad_accumulate(acc, grads[s], False)
 
     sweep_only = [("layernorm_residual_fwd", lnr_fwd_set, 4), ("layernorm_residual_bwd", lnr_bwd_set, 4),
                   ("alibi_attention_fwd", att_fwd_set, 4), ("alibi_attention_fwd_8192", att_fwd_long_set, 2),
-                  ("alibi_attention_bwd", att_bwd_set, 4)]
+                  ("alibi_attention_bwd", att_bwd_set, 4), ("layernorm_fwd_8192", ln_fwd_long_set, 4),
+                  ("alibi_softmax_fwd_8192", sm_fwd_long_set, 2)]
     if batch > 1:
         sweep_only.append(("grad_accumulate", acc_one_set, nbuf))
 
@@ -384,9 +414,7 @@ def run_gpu(args):
         del fns
     shapes = {"ln": (rows, hid), "sm": (smb, smh, sms), "gelu": (grows, gcols), "head_dim": hd}
     bts = bytes_model(shapes, n, mb, batch)
-    lb, lh, ls, ld = L.batch, L.heads, L.seq, L.head_dim
-    bts["alibi_attention_fwd_8192"] = lb * lh * ls * ld * 2 * 4 + lb * lh * ls * 4
-    bts["_attention_flops_8192"] = 2 * 2 * lb * lh * (ls * (ls + 1) // 2) * ld
+    bts.update(long_context_model(W.LONG.ln.rows, W.LONG.ln.hidden, L.batch, L.heads, L.seq, L.head_dim))
     return ms_step, in_step, sweep, sweep_min, bts, n, mb
 
 

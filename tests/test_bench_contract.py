@@ -98,3 +98,15 @@ def test_committed_counters_match_the_current_source():
     assert "grad_accumulate_many_last" in data
     for key, entry in data.items():
         assert entry["source_digest"] == bench.source_digest(*entry["sources"]), key
+
+
+def test_long_context_rows():
+    m = bench.long_context_model(8192, H, 1, NH, 8192, D)
+    assert m["layernorm_fwd_8192"] == 8192 * H * 2 * 2 + H * 2 * 2 + 8192 * 4 * 2
+    causal = NH * 8192 * 8193 // 2
+    assert m["alibi_softmax_fwd_8192"] == causal * 2 + NH * 8192 * 8192 * 2
+    assert m["alibi_attention_fwd_8192"] == NH * 8192 * D * 2 * 4 + NH * 8192 * 4
+    assert m["_attention_flops_8192"] == causal * D * 2 * 2
+    assert round(m["layernorm_fwd_8192"] / 1e6, 1) == 469.9
+    assert round(m["alibi_softmax_fwd_8192"] / 1e9, 2) == 5.64
+    assert round(m["_attention_flops_8192"] / 1e9, 2) == 481.10
