@@ -106,6 +106,18 @@ def long_context_model(ln_rows, hidden, batch, heads, seq, head_dim):
     }
 
 
+def mini_model():
+    """Algorithmic bytes of the mini-BLOOM rows (the same models at the mini shapes)."""
+    from synth import workloads as W
+    mi = W.MINI
+    shapes = {"ln": (mi.ln.rows, mi.ln.hidden), "sm": (mi.softmax.batch, mi.softmax.heads, mi.softmax.seq),
+              "gelu": (mi.gelu.rows, mi.gelu.cols), "head_dim": mi.softmax.head_dim}
+    m = bytes_model(shapes, mi.opt.n, 32)
+    keys = ("layernorm_fwd", "layernorm_bwd", "alibi_softmax_fwd", "alibi_softmax_bwd", "bias_gelu_fwd",
+            "bias_gelu_bwd", "adamw_step")
+    return {k + "_mini": m[k] for k in keys}
+
+
 def source_digest(*paths):
     h = hashlib.sha256()
     for p in paths:
@@ -296,6 +308,71 @@ def run_gpu(args):
         p = torch.empty_like(sc)
         return lambda: ops.bloom_alibi_softmax_fwd(sc, p, ls.head_offset, ls.total_heads, ls.scale)
 
+    # The mini-BLOOM layer (hidden 2048, 16 heads, FFN 8192, seq 2048, micro-batch 4): sweep-only rows.
+    MI = W.MINI
+    mrows, mhid = MI.ln.rows, MI.ln.hidden
+    msm = MI.softmax
+    mgrows, mgcols = MI.gelu.rows, MI.gelu.cols
+    m_g = fill((mhid,), W.S_LN_GAMMA, 0.02, 1.0)
+    m_b = fill((mhid,), W.S_LN_BETA, 0.02)
+    m_gb = fill((mgcols,), W.S_GELU_BIAS, 0.02)
+
+    def m_ln_fwd_set(s):
+        x = fill((mrows, mhid), W.S_LN_X, 1.0, s=s)
+        y = torch.empty_like(x)
+        m = torch.empty(mrows, dtype=f32, device=dev)
+        r = torch.empty_like(m)
+        return lambda: ops.bloom_layernorm_fwd(x, m_g, m_b, y, m, r, W.LN_EPS)
+
+    def m_ln_bwd_set(s):
+        x = fill((mrows, mhid), 50, 1.0, s=s)
+        dy = fill((mrows, mhid), W.S_LN_DY, 1.0, s=s)
+        dx = torch.empty_like(x)
+        m = torch.empty(mrows, dtype=f32, device=dev)
+        r = torch.empty_like(m)
+        ops.bloom_layernorm_fwd(x, m_g, m_b, dx, m, r, W.LN_EPS)
+        dg, db = torch.empty(mhid, dtype=bf, device=dev), torch.empty(mhid, dtype=bf, device=dev)
+        ws = torch.empty(ops.bloom_layernorm_bwd_workspace_size(mrows, mhid), dtype=torch.uint8, device=dev)
+        return lambda: ops.bloom_layernorm_bwd(dy, x, m_g, m, r, dx, dg, db, ws)
+
+    def m_sm_fwd_set(s):
+        sc = fill((msm.batch, msm.heads, msm.seq, msm.seq), W.S_SM_SCORES, 1.0, s=s)
+        p = torch.empty_like(sc)
+        return lambda: ops.bloom_alibi_softmax_fwd(sc, p, msm.head_offset, msm.total_heads, msm.scale)
+
+    def m_sm_bwd_set(s):
+        sc = fill((msm.batch, msm.heads, msm.seq, msm.seq), 51, 1.0, s=s)
+        y = torch.empty_like(sc)
+        ops.bloom_alibi_softmax_fwd(sc, y, msm.head_offset, msm.total_heads, msm.scale)
+        del sc
+        dy = fill((msm.batch, msm.heads, msm.seq, msm.seq), W.S_SM_DPROBS, 1.0, s=s)
+        ds = torch.empty_like(y)
+        return lambda: ops.bloom_alibi_softmax_bwd(y, dy, ds, msm.scale)
+
+    def m_ge_fwd_set(s):
+        x = fill((mgrows, mgcols), W.S_GELU_X, 1.0, s=s)
+        y = torch.empty_like(x)
+        return lambda: ops.bloom_bias_gelu_fwd(x, m_gb, y)
+
+    def m_ge_bwd_set(s):
+        x = fill((mgrows, mgcols), 52, 1.0, s=s)
+        dy = fill((mgrows, mgcols), W.S_GELU_DY, 1.0, s=s)
+        dx = torch.empty_like(x)
+        db = torch.empty(mgcols, dtype=bf, device=dev)
+        ws = torch.empty(ops.bloom_bias_gelu_bwd_workspace_size(mgrows, mgcols), dtype=torch.uint8, device=dev)
+        return lambda: ops.bloom_bias_gelu_bwd(dy, x, m_gb, dx, db, ws)
+
+    def m_adamw_set(s):
+        # the mini model's 1,722,400,768 parameters as slices of the shard's buffers (timed after the
+        # steps); one accumulation pass over the slice leaves the norm's partial sums in the workspace
+        nm = MI.opt.n
+        ws = torch.empty(ops.bloom_bf16_adamw_workspace_size(nm), dtype=torch.uint8, device=dev)
+        ops.bloom_bf16_grad_accumulate_sumsq(acc[:nm], grads[0][:nm], True, ws)
+        hp = ops.adamw_hparams(W.LR, W.BETA1, W.BETA2, W.ADAM_EPS, W.WEIGHT_DECAY, W.MAX_GRAD_NORM, MI.opt.step,
+                               sumsq_in_workspace=True)
+        return lambda: ops.bloom_bf16_adamw_step(master[:nm], exp_avg[:nm], exp_avg_sq[:nm], param[:nm], acc[:nm], hp,
+                                                 norm, ws)
+
     def acc_one_set(s):
         # one micro-batch per pass (a later micro-batch), over the resident gradient buffers
         return lambda: ops.bloom_bf16_grad_accumulate(acc, grads[s], False)
@@ -303,7 +380,12 @@ def run_gpu(args):
     sweep_only = [("layernorm_residual_fwd", lnr_fwd_set, 4), ("layernorm_residual_bwd", lnr_bwd_set, 4),
                   ("alibi_attention_fwd", att_fwd_set, 4), ("alibi_attention_fwd_8192", att_fwd_long_set, 2),
                   ("alibi_attention_bwd", att_bwd_set, 4), ("layernorm_fwd_8192", ln_fwd_long_set, 4),
-                  ("alibi_softmax_fwd_8192", sm_fwd_long_set, 2)]
+                  ("alibi_softmax_fwd_8192", sm_fwd_long_set, 2),
+                  ("layernorm_fwd_mini", m_ln_fwd_set, 4), ("layernorm_bwd_mini", m_ln_bwd_set, 4),
+                  ("alibi_softmax_fwd_mini", m_sm_fwd_set, 2), ("alibi_softmax_bwd_mini", m_sm_bwd_set, 2),
+                  ("bias_gelu_fwd_mini", m_ge_fwd_set, 4), ("bias_gelu_bwd_mini", m_ge_bwd_set, 4)]
+    if n >= MI.opt.n:   # the mini model's update runs on slices of the shard's buffers
+        sweep_only.append(("adamw_step_mini", m_adamw_set, 1))
     if batch > 1:
         sweep_only.append(("grad_accumulate", acc_one_set, nbuf))
 
@@ -415,6 +497,7 @@ def run_gpu(args):
     shapes = {"ln": (rows, hid), "sm": (smb, smh, sms), "gelu": (grows, gcols), "head_dim": hd}
     bts = bytes_model(shapes, n, mb, batch)
     bts.update(long_context_model(W.LONG.ln.rows, W.LONG.ln.hidden, L.batch, L.heads, L.seq, L.head_dim))
+    bts.update(mini_model())
     return ms_step, in_step, sweep, sweep_min, bts, n, mb
 
 

@@ -110,3 +110,17 @@ def test_long_context_rows():
     assert round(m["layernorm_fwd_8192"] / 1e6, 1) == 469.9
     assert round(m["alibi_softmax_fwd_8192"] / 1e9, 2) == 5.64
     assert round(m["_attention_flops_8192"] / 1e9, 2) == 481.10
+
+
+def test_mini_rows():
+    m = bench.mini_model()
+    rows, hid, heads, seq, ffn = 4 * 2048, 2048, 16, 2048, 8192
+    causal = 4 * heads * seq * (seq + 1) // 2
+    assert m["layernorm_fwd_mini"] == rows * hid * 4 + hid * 4 + rows * 8
+    assert m["layernorm_bwd_mini"] == rows * hid * 6 + hid * 2 + rows * 8 + hid * 4
+    assert m["alibi_softmax_fwd_mini"] == causal * 2 + 4 * heads * seq * seq * 2
+    assert m["alibi_softmax_bwd_mini"] == causal * 4 + 4 * heads * seq * seq * 2
+    assert m["bias_gelu_fwd_mini"] == rows * ffn * 4 + ffn * 2
+    assert m["bias_gelu_bwd_mini"] == rows * ffn * 6 + ffn * 4
+    n_mini = 24 * (12 * hid ** 2 + 13 * hid) + 250880 * hid     # 24 layers plus the embedding
+    assert n_mini == 1_722_400_768 and m["adamw_step_mini"] == n_mini * 30
