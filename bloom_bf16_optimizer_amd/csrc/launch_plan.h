@@ -91,10 +91,27 @@ inline RowPlan plan_rows_fwd(int64_t rows, int vecs) {
 }
 
 // Backward: one workgroup per compute unit at most (the column partial rows
-// it writes scale with the grid), teams walk rows with stride grid*teams.
+// it writes scale with the grid; two for H = 2048, below), teams walk rows
+// with stride grid*teams.
 inline RowPlan plan_rows_bwd(int64_t rows, int vecs, int cus) {
   RowPlan p;
   pick_team(vecs, 4, p.tpr, p.nv);
+  if (vecs == 256) {
+    // H = 2048: a four-wave team per row, one vector per thread (the streaming
+    // kernel), two workgroups per compute unit.  The wave-per-row form holds a
+    // row's 32 elements per lane at 210 registers, two waves per SIMD, and its
+    // arithmetic per wave is then as long as its memory time.  Measured at
+    // [8192, 2048]: 46.2 -> 29.9 us; [16384, 2048] 64.1 -> 47.3; [2048, 2048]
+    // 22.6 -> 15.4 (one workgroup per unit: 40.4, 72.0, 16.3; four: 31.1,
+    // 48.4, 18.3).
+    p.tpr = 256;
+    p.nv = 1;
+    p.block = p.tpr;
+    const int64_t g = (int64_t)cus * 2;
+    p.grid = (int)(rows < g ? rows : g);
+    if (p.grid < 1) p.grid = 1;
+    return p;
+  }
   if (p.tpr == 64) {
     // A wave per row: eight rows in flight per workgroup (the eight waves'
     // column sums are added in LDS, still one partial row per workgroup)
