@@ -2,7 +2,8 @@
 
 * ``bloom_bf16_optimizer_amd/libbloomkern.so`` -- the kernels and their C ABI
   (``include/bloom_kernels.h``), from ``bloom_bf16_optimizer_amd/csrc``.
-* ``synth/libbloomsynth.so`` -- the device side of the seeded input generator.
+* ``synth/libbloomsynth.so`` -- the device side of the seeded input generator,
+  and a plain streaming copy that ``bench.py`` times as the bandwidth ceiling.
 
 Run ``python -m bloom_bf16_optimizer_amd.build`` (or ``__graft_entry__.build()``).
 """
@@ -63,15 +64,16 @@ def build(verbose: bool = True) -> list[str]:
     jobs = []
     for s in kern_srcs:
         jobs.append((s, os.path.join(BUILD, "k_" + os.path.basename(s) + ".o"), []))
-    synth_src = os.path.join(ROOT, "synth", "csrc", "synth.hip")
-    jobs.append((synth_src, os.path.join(BUILD, "s_synth.o"), ["-ffp-contract=off"]))
+    synth_srcs = sorted(glob.glob(os.path.join(ROOT, "synth", "csrc", "*.hip")))
+    for s in synth_srcs:
+        jobs.append((s, os.path.join(BUILD, "s_" + os.path.basename(s) + ".o"), ["-ffp-contract=off"]))
     workers = min(8, os.cpu_count() or 4, len(jobs))
     with cf.ThreadPoolExecutor(max_workers=workers) as ex:
         futs = [ex.submit(_compile, s, o, e) for s, o, e in jobs]
         for f in futs:
             f.result()
-    _link([o for s, o, _ in jobs if s != synth_src], LIB_KERNELS)
-    _link([os.path.join(BUILD, "s_synth.o")], LIB_SYNTH)
+    _link([o for s, o, _ in jobs if s not in synth_srcs], LIB_KERNELS)
+    _link([o for s, o, _ in jobs if s in synth_srcs], LIB_SYNTH)
     if verbose:
         print(f"built {LIB_KERNELS}\nbuilt {LIB_SYNTH}")
     return [LIB_KERNELS, LIB_SYNTH]

@@ -27,6 +27,11 @@ Definition (the device kernel implements exactly the same steps):
 
 Approximate normality is all that is needed: the values have the mean and
 standard deviation of the workloads and a support of +-6 sigma.
+
+The device library (``synth/csrc``) also holds a plain streaming copy
+(``synth/csrc/ceiling.hip``, ``synth.device.stream_copy``) that the benchmark
+times as the bandwidth ceiling of each read/write pattern; like the generator,
+it computes nothing of the method.
 """
 
 from __future__ import annotations

@@ -27,6 +27,10 @@ def _load():
         lib.synth_fill.restype = ctypes.c_int
         lib.synth_fill.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_uint64,
                                    ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        lib.synth_stream_copy.restype = ctypes.c_int
+        lib.synth_stream_copy.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                          ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int64,
+                                          ctypes.c_void_p]
         _lib = lib
     return _lib
 
@@ -53,3 +57,23 @@ def _fill(t, seed, stream, sigma, offset, start, mode):
     if rc != 0:
         raise RuntimeError(f"synth_fill failed with code {rc}")
     return t
+
+
+def stream_copy(outs, ins) -> None:
+    """Plain streaming copy (the bandwidth ceiling bench.py compares kernels with).
+
+    ``outs`` (1 or 2) and ``ins`` (1 or 2) are contiguous GPU tensors of one
+    common byte size, a multiple of 16; every output receives the XOR of the
+    inputs (a copy for one input).  Enqueued on the current stream.
+    """
+    nbytes = outs[0].numel() * outs[0].element_size()
+    for t in (*outs, *ins):
+        if not (t.is_cuda and t.is_contiguous()) or t.numel() * t.element_size() != nbytes:
+            raise ValueError("stream_copy needs contiguous GPU tensors of one byte size")
+    if nbytes % 16:
+        raise ValueError("stream_copy needs a multiple of 16 bytes")
+    o = (ctypes.c_void_p * len(outs))(*[t.data_ptr() for t in outs])
+    i = (ctypes.c_void_p * len(ins))(*[t.data_ptr() for t in ins])
+    rc = _load().synth_stream_copy(o, len(outs), i, len(ins), nbytes // 16, torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_stream_copy failed with code {rc}")

@@ -63,6 +63,37 @@ def test_optimizer_bytes(batch):
         assert m["grad_accumulate_many_last"] == 146_800_000_000
 
 
+def test_step_bytes_one_pass_per_micro_batch():
+    """The headline step: six fused kernels, then one accumulation pass per
+    micro-batch (6 B per element for the first, 10 B for each of the other 31)
+    and the 30 B per element AdamW step."""
+    m = _model(16)
+    fused = sum(m[k] for k in ("layernorm_fwd", "layernorm_bwd", "alibi_softmax_fwd", "alibi_softmax_bwd",
+                               "bias_gelu_fwd", "bias_gelu_bwd"))
+    assert bench.step_bytes(m, 32) == fused + N * (6 + 31 * 10 + 30)
+    assert round((bench.step_bytes(m, 32) - fused) / 1e12, 3) == 1.270
+
+
+def test_copy_ceiling_patterns():
+    """Each kernel's ceiling copies what it reads and writes."""
+    pat = bench.copy_patterns({"ln": (R, H), "sm": (B, NH, L), "gelu": (R, H), "head_dim": D}, N)
+    assert pat["1in_1out_act"] == (1, 1, R * H * 2)
+    assert pat["2in_1out_act"] == (2, 1, R * H * 2)
+    causal = B * NH * L * (L + 1) // 2 * 2
+    assert pat["1in_2out_causal"][:2] == (1, 2) and causal - 16 < pat["1in_2out_causal"][2] <= causal
+    assert pat["2in_2out_causal"][:2] == (2, 2)
+    assert pat["1in_1out_fp32_shard"] == (1, 1, N * 4)
+    for k, c in bench.CEILING_OF.items():
+        assert c in pat, k
+
+
+def test_cpu_share_respects_the_thread_allotment(monkeypatch):
+    monkeypatch.setenv("OMP_NUM_THREADS", "3")
+    assert 1 <= bench.cpu_share() <= 3
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert bench.cpu_share() >= 1
+
+
 def _run(*args):
     return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
                           timeout=120)
@@ -73,7 +104,7 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
 
 
-@pytest.mark.parametrize("batch", ["3", "0", "17", "32"])
+@pytest.mark.parametrize("batch", ["3", "1", "17", "32", "-1"])
 def test_accumulation_batch_must_split_the_32_micro_batches(batch):
     r = _run("--accum-batch", batch)
     assert r.returncode == 2 and "--accum-batch" in r.stderr

@@ -83,9 +83,10 @@ def test_layernorm_residual_workloads_full(wl):
 # (600, 8192) and (777, 5120): streaming backward with a dres slot (2 and 1
 # vectors per thread); (7, 16384): a 16-wave team whose ring + dres slot does
 # not fit in LDS, so the generic backward; (5, 4104), (3, 1000): generic
-# block and wave teams.
+# block and wave teams; (600, 2048), (777, 2048): the four-wave team at
+# H = 2048, two workgroups per compute unit, 1 or 2 rows per workgroup.
 @pytest.mark.parametrize("rows,hidden", [(600, 8192), (777, 5120), (7, 16384), (5, 4104), (3, 1000), (1, 8),
-                                         (2, 65536)])
+                                         (2, 65536), (600, 2048), (777, 2048)])
 def test_layernorm_residual_ragged(rows, hidden):
     require_gpu()
     _check(f"ragged {rows}x{hidden}", *_inputs(21, rows, hidden))

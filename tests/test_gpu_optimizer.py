@@ -319,6 +319,47 @@ def test_shard_optimizer_full_size():
                   host_bf16(param[ti]), f64, terms, rpb)
 
 
+@pytest.mark.timeout(1200)
+def test_shard_accumulate_many_full_size():
+    """The batched accumulation at the 3.67e9-element shard: 32 distinct
+    micro-batch gradients in two passes of 16 resident gradients (the second
+    with the norm partials).  Sampled elements, including indices on both
+    sides of 2^31, are bit-exact against the oracle's sequential FP32 adds;
+    the fused norm partials give the step the float64 norm of the full
+    accumulator within 1e-6."""
+    require_gpu()
+    wl = W.OPTIMIZER
+    n, mb, k = wl.opt.n, wl.opt.microbatches, 16
+    ws = _workspace(n)
+    acc = torch.empty(n, dtype=torch.float32, device="cuda")
+    grads = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(k)]
+    for p0 in range(0, mb, k):
+        for j in range(k):
+            sdev.fill_(grads[j], wl.seed, W.S_OPT_GRAD0 + 1 + p0 + j, W.GRAD_SIGMA)
+        last = p0 + k == mb
+        ops.bloom_bf16_grad_accumulate_many(acc, grads, p0 == 0, ws if last else None)
+    torch.cuda.synchronize()
+    del grads
+    idx = sample_rows(n, 300_000, 47, must=list(range(8)) + list(range(n - 8, n))
+                      + [2 ** 31 - 1, 2 ** 31, 2 ** 31 + 1, 3 * 2 ** 30, 3 * 2 ** 30 + 1, 3_600_000_000])
+    ti = torch.from_numpy(idx).cuda()
+    got = acc[ti].cpu().numpy()
+    ref = _accumulate_oracle(idx.astype(np.uint64), wl.seed, mb)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), "accumulator not bit-exact"
+    ss = 0.0
+    chunk = 1 << 28
+    for i in range(0, n, chunk):
+        a = acc[i:i + chunk].cpu().numpy().astype(np.float64)
+        ss += float(np.dot(a, a))
+    rnorm = float(np.sqrt(ss))
+    tp = gen((n,), wl.seed, W.S_OPT_PARAM, W.PARAM_SIGMA, dtype=torch.float32)[0]
+    tm = torch.zeros(n, dtype=torch.float32, device="cuda")
+    tv = torch.zeros(n, dtype=torch.float32, device="cuda")
+    _, norm = _step_gpu(tp, tm, tv, acc, _hp(1, sumsq_in_workspace=True), ws=ws)
+    assert abs(norm - rnorm) <= 1e-6 * rnorm, (norm, rnorm)
+    assert 330.0 < norm < 355.0   # 32 distinct N(0, 1e-3) gradients: about 342.7
+
+
 @pytest.mark.parametrize("n,segs,fused", [
     (1_000_003, [(0, 600_000, 0.01), (600_000, 300_000, 0.0), (900_000, 100_003, 0.05)], False),
     (1_000_003, [(0, 999_992, 0.01), (999_992, 11, 0.0)], True),
