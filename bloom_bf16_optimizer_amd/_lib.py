@@ -41,6 +41,7 @@ SIGNATURES = {
     "bloom_layernorm_fwd": (ctypes.c_int, [c_void_p] * 6 + [c_i64, c_i64, c_f32, c_void_p]),
     "bloom_layernorm_bwd_workspace_size": (c_size, [c_i64, c_i64]),
     "bloom_layernorm_bwd": (ctypes.c_int, [c_void_p] * 9 + [c_size, c_i64, c_i64, c_void_p]),
+    "bloom_layernorm_bwd_noalloc": (ctypes.c_int, [c_void_p] * 8 + [c_i64, c_i64, c_void_p]),
     "bloom_layernorm_residual_fwd": (ctypes.c_int, [c_void_p] * 8 + [c_i64, c_i64, c_f32, c_void_p]),
     "bloom_layernorm_residual_bwd": (ctypes.c_int, [c_void_p] * 10 + [c_size, c_i64, c_i64, c_void_p]),
     "bloom_alibi_slopes": (ctypes.c_int, [c_i32, c_i32, c_i32, ctypes.POINTER(c_f32)]),

@@ -55,7 +55,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int bloom_abi_version(void) { return 7; }
+int bloom_abi_version(void) { return 8; }
 
 const char* bloom_status_string(int status) {
   switch (status) {

@@ -18,9 +18,16 @@
 // columns it owns while its team walks a strided set of rows, combines the
 // teams of a workgroup in LDS, and writes one FP32 partial row per workgroup;
 // colsum_kernel (colsum.hip) adds the partial rows in a fixed order.
+#include <mutex>
+
 #include "device_common.h"
 #include "host_common.h"
 #include "launch_plan.h"
+
+// Scratch of bloom_layernorm_bwd_noalloc: its column partial rows live here
+// instead of in a caller workspace.  One copy per device, held until the
+// process ends; every call on a device shares it.
+static __device__ __align__(256) unsigned char scratch[BLOOM_NOALLOC_SCRATCH_BYTES];
 
 namespace bloom {
 namespace {
@@ -694,6 +701,63 @@ extern "C" bloom_status bloom_layernorm_bwd(const bloom_bf16* dy, const bloom_bf
   clear_error();
   return layernorm_bwd_impl<false>("bloom_layernorm_bwd", dy, x, nullptr, gamma, mean, rstd, dx, dgamma,
                                    dbeta, workspace, workspace_bytes, rows, hidden, stream);
+}
+
+namespace bloom {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device of `stream`, looked up once
+// per device with that device current.  In host code `scratch` names a host
+// stand-in, so only this address may reach a kernel.
+bloom_status scratch_address(hipStream_t stream, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(BLOOM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  hipDevice_t sdev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return fail(BLOOM_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+  }
+  BLOOM_REQUIRE(sdev == cur, BLOOM_ERR_HPARAM,
+                "stream belongs to device %d but device %d is current; make the stream's device current", (int)sdev,
+                cur);
+  BLOOM_REQUIRE(cur >= 0 && cur < kMaxDevices, BLOOM_ERR_HIP, "device %d beyond the %d supported", cur, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[cur] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(BLOOM_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", cur, hipGetErrorString(e));
+    g_scratch_ptr[cur] = p;
+  }
+  *out = g_scratch_ptr[cur];
+  return BLOOM_OK;
+}
+
+}  // namespace
+}  // namespace bloom
+
+extern "C" bloom_status bloom_layernorm_bwd_noalloc(const bloom_bf16* dy, const bloom_bf16* x,
+                                                    const bloom_bf16* gamma, const float* mean,
+                                                    const float* rstd, bloom_bf16* dx, bloom_bf16* dgamma,
+                                                    bloom_bf16* dbeta, int64_t rows, int64_t hidden,
+                                                    hipStream_t stream) {
+  clear_error();
+  if (bloom_status st = check_rows(rows, hidden)) return st;
+  if (rows == 0) return BLOOM_OK;
+  const size_t need = bloom_layernorm_bwd_workspace_size(rows, hidden);
+  BLOOM_REQUIRE(need <= (size_t)BLOOM_NOALLOC_SCRATCH_BYTES, BLOOM_ERR_WORKSPACE,
+                "rows = %lld, hidden = %lld need %zu bytes of scratch; the static scratch holds %zu "
+                "(use bloom_layernorm_bwd with a workspace)",
+                (long long)rows, (long long)hidden, need, (size_t)BLOOM_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (bloom_status st = scratch_address(stream, &ws)) return st;
+  return layernorm_bwd_impl<false>("bloom_layernorm_bwd_noalloc", dy, x, nullptr, gamma, mean, rstd, dx, dgamma,
+                                   dbeta, ws, (size_t)BLOOM_NOALLOC_SCRATCH_BYTES, rows, hidden, stream);
 }
 
 extern "C" bloom_status bloom_layernorm_residual_bwd(const bloom_bf16* dy, const bloom_bf16* dres,

@@ -90,6 +90,22 @@ def bloom_layernorm_bwd(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace) 
         _stream()))
 
 
+def bloom_layernorm_bwd_noalloc(dy, x, gamma, mean, rstd, dx, dgamma, dbeta) -> None:
+    """bloom_layernorm_bwd without a workspace (the library's static scratch)."""
+    rows, hidden = _rows_cols(x)
+    _same(x, dy, "x/dy")
+    _same(x, dx, "x/dx")
+    if gamma.numel() != hidden or dgamma.numel() != hidden or dbeta.numel() != hidden:
+        raise ValueError("gamma/dgamma/dbeta must have `hidden` elements")
+    if mean.numel() != rows or rstd.numel() != rows:
+        raise ValueError("mean/rstd must have `rows` elements")
+    lib = _lib.load()
+    check("bloom_layernorm_bwd_noalloc", lib.bloom_layernorm_bwd_noalloc(
+        _ptr(dy, BF16, "dy"), _ptr(x, BF16, "x"), _ptr(gamma, BF16, "gamma"), _ptr(mean, F32, "mean"),
+        _ptr(rstd, F32, "rstd"), _ptr(dx, BF16, "dx"), _ptr(dgamma, BF16, "dgamma"),
+        _ptr(dbeta, BF16, "dbeta"), rows, hidden, _stream()))
+
+
 def bloom_layernorm_residual_fwd(x, residual, gamma, beta, h, y, mean, rstd, eps: float) -> None:
     rows, hidden = _rows_cols(x)
     for t, name in ((residual, "residual"), (h, "h"), (y, "y")):

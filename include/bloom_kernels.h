@@ -17,6 +17,8 @@
  *   PyTorch).  The library never allocates, frees or synchronises; a call only
  *   validates its arguments and enqueues kernels on `stream` (NULL = the
  *   default stream).  Outputs are complete once the stream reaches that point.
+ *   (bloom_layernorm_bwd_noalloc is the one entry point with memory of its
+ *   own: a static device array, see there.)
  * - bf16 values are raw bfloat16 bit patterns (`bloom_bf16`).  All arithmetic
  *   is FP32 (FP64 for the gradient-norm sum); bf16 outputs are rounded to
  *   nearest, ties to even.
@@ -103,6 +105,32 @@ bloom_status bloom_layernorm_bwd(const bloom_bf16* dy, const bloom_bf16* x,
                                  const float* rstd, bloom_bf16* dx, bloom_bf16* dgamma,
                                  bloom_bf16* dbeta, void* workspace, size_t workspace_bytes,
                                  int64_t rows, int64_t hidden, hipStream_t stream);
+
+/* Size of the static device scratch of bloom_layernorm_bwd_noalloc (32 MiB
+ * per device). */
+#define BLOOM_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* bloom_layernorm_bwd for callers that cannot allocate memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels and results (bit for bit) as bloom_layernorm_bwd,
+ * without the workspace: the column partial sums go to a static device array
+ * of BLOOM_NOALLOC_SCRATCH_BYTES that each device holds from the library's
+ * load until the process ends.  The call allocates nothing.
+ *   - rows, hidden whose bloom_layernorm_bwd_workspace_size exceeds
+ *     BLOOM_NOALLOC_SCRATCH_BYTES -> BLOOM_ERR_WORKSPACE (with 256 compute
+ *     units: any rows at hidden <= 16384; BLOOM-176B's 14336 needs 28 MiB);
+ *   - `stream` must belong to the current device, else BLOOM_ERR_HPARAM;
+ *   - the first call on a device looks the array's device address up
+ *     (hipGetSymbolAddress) and keeps it; a failure -> BLOOM_ERR_HIP.
+ * Every call on one device shares the one array and leaves its contents
+ * behind (nothing in it needs to start at zero).  Calls that overlap on one
+ * device -- on different streams, or from different threads -- race on it
+ * and must not be issued. */
+bloom_status bloom_layernorm_bwd_noalloc(const bloom_bf16* dy, const bloom_bf16* x,
+                                         const bloom_bf16* gamma, const float* mean,
+                                         const float* rstd, bloom_bf16* dx, bloom_bf16* dgamma,
+                                         bloom_bf16* dbeta, int64_t rows, int64_t hidden,
+                                         hipStream_t stream);
 
 /* LayerNorm fused with the residual connection, forward.  [3d] 4.3 (a fused
  * LayerNorm + residual kernel, printed there as a stub); the LayerNorm is the

@@ -53,7 +53,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.bloom_abi_version() == 7
+    assert lib.bloom_abi_version() == 8
     assert lib.bloom_status_string(0) == b"ok"
     assert lib.bloom_status_string(4) == b"workspace too small"
     assert lib.bloom_status_string(99) == b"unknown status"
@@ -98,6 +98,20 @@ def test_layernorm_validation(lib):
     assert b(p, p, p, p, p, p, p, p, p, 16, 4, 16, None) == WORKSPACE
     assert b(p, p, p, p, p, p, p, p, p + 4, 1 << 20, 4, 16, None) == ALIGN
     assert lib.bloom_layernorm_bwd_workspace_size(4, 12) == 0
+
+
+def test_layernorm_noalloc_validation(lib):
+    """The allocation-free backward: host checks before any scratch lookup or launch."""
+    p = FAKE
+    f = lib.bloom_layernorm_bwd_noalloc
+    assert f(p, p, p, p, p, p, p, p, 4, 12, None) == SHAPE
+    assert f(p, p, p, p, p, p, p, p, 0, 16, None) == OK               # empty: no-op
+    # 256 partial rows of 2 x 65536 floats (128 MiB) exceed the 32 MiB static scratch
+    assert lib.bloom_layernorm_bwd_workspace_size(2048, 65536) > (32 << 20)
+    assert f(p, p, p, p, p, p, p, p, 2048, 65536, None) == WORKSPACE
+    assert b"scratch" in lib.bloom_last_error()
+    # BLOOM-176B's width fits
+    assert lib.bloom_layernorm_bwd_workspace_size(2048, 14336) <= (32 << 20)
 
 
 def test_layernorm_residual_validation(lib):
