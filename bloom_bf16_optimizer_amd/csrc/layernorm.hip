@@ -48,15 +48,28 @@ __device__ __forceinline__ uint4 add_bf16x8(const uint4& a, const uint4& b) {
 }
 
 // RES: the residual form -- h = bf16(x + res) is formed on load, written to
-// h_out, and normalised in place of x.
-template <int NV, int MAXB, bool RES>
-__global__ __launch_bounds__(MAXB) void ln_fwd_kernel(
+// h_out, and normalised in place of x.  WAVE: one wave per row (tpr == 64);
+// otherwise the workgroup is the row team.  EXACT: the team covers the row
+// with no idle lane (tpr * NV == vecs), so no vector needs a bounds guard,
+// and a block team is exactly MAXB threads, so its width is a constant.
+// Both are template parameters, not run-time branches: each kernel holds only
+// its own reduction and index arithmetic.  WPE: the waves per SIMD the
+// register allocation must allow (1: no constraint).  At H = 14336 (256 x 7)
+// the block-team kernel fits 95 VGPRs with WPE = 5, five one-row workgroups
+// per compute unit instead of four: [2048, 14336] 23.8-24.4 -> 22.7-22.9 us
+// in one process; at [8192, 14336] the two are within run-to-run spread
+// (84.1-85.2 us either way).
+template <int NV, int MAXB, bool RES, bool WAVE, bool EXACT, int WPE>
+__global__ __launch_bounds__(MAXB) __attribute__((amdgpu_waves_per_eu(WPE)))
+void ln_fwd_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ res, uint4* __restrict__ h_out,
     const uint4* __restrict__ gamma, const uint4* __restrict__ beta,
     uint4* __restrict__ y, float* __restrict__ mean, float* __restrict__ rstd, int64_t rows,
-    int vecs, int tpr, float hidden, float eps) {
+    int vecs_arg, int tpr_arg, float hidden, float eps) {
   __shared__ float lds[kMaxWaves];
-  const bool wave_rows = (tpr == kWave);
+  constexpr bool wave_rows = WAVE;
+  const int tpr = WAVE ? kWave : (EXACT ? MAXB : tpr_arg);
+  const int vecs = EXACT ? tpr * NV : vecs_arg;
   const int t = wave_rows ? (int)(threadIdx.x & (kWave - 1)) : (int)threadIdx.x;
   const int64_t row = wave_rows
                           ? (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave
@@ -72,20 +85,20 @@ __global__ __launch_bounds__(MAXB) void ln_fwd_kernel(
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     const int v = t + k * tpr;
-    xv[k] = (v < vecs) ? ld_nt(xr + v) : make_uint4(0u, 0u, 0u, 0u);
+    xv[k] = (EXACT || v < vecs) ? ld_nt(xr + v) : make_uint4(0u, 0u, 0u, 0u);
   }
   if (RES) {
     uint4 rv[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int v = t + k * tpr;
-      rv[k] = (v < vecs) ? ld_nt(res + row * vecs + v) : make_uint4(0u, 0u, 0u, 0u);
+      rv[k] = (EXACT || v < vecs) ? ld_nt(res + row * vecs + v) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int v = t + k * tpr;
       xv[k] = add_bf16x8(xv[k], rv[k]);
-      if (v < vecs) st_nt(h_out + row * vecs + v, xv[k]);
+      if (EXACT || v < vecs) st_nt(h_out + row * vecs + v, xv[k]);
     }
   }
 
@@ -103,7 +116,7 @@ __global__ __launch_bounds__(MAXB) void ln_fwd_kernel(
   float q = 0.f;
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    if (t + k * tpr < vecs) {
+    if (EXACT || t + k * tpr < vecs) {
       float f[8];
       unpack8(xv[k], f);
 #pragma unroll
@@ -120,7 +133,7 @@ __global__ __launch_bounds__(MAXB) void ln_fwd_kernel(
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     const int v = t + k * tpr;
-    if (v < vecs) {
+    if (EXACT || v < vecs) {
       float f[8], g[8], b[8], o[8];
       unpack8(xv[k], f);
       unpack8(gamma[v], g);
@@ -556,8 +569,18 @@ template <int NV, int MAXB, bool RES>
 void launch_fwd(const RowPlan& p, hipStream_t s, const uint4* x, const uint4* res, uint4* h,
                 const uint4* g, const uint4* b, uint4* y, float* mean, float* rstd, int64_t rows,
                 int vecs, float eps) {
-  hipLaunchKernelGGL((ln_fwd_kernel<NV, MAXB, RES>), dim3(p.grid), dim3(p.block), 0, s, x, res, h, g, b, y,
-                     mean, rstd, rows, vecs, p.tpr, (float)(vecs * 8), eps);
+  const bool exact = p.tpr * NV == vecs && (p.tpr == kWave || p.tpr == MAXB);
+#define BLOOM_LN_FWD(WAVE, EXACT, WPE)                                                                          \
+  hipLaunchKernelGGL((ln_fwd_kernel<NV, MAXB, RES, WAVE, EXACT, WPE>), dim3(p.grid), dim3(p.block), 0, s, x, res, h, \
+                     g, b, y, mean, rstd, rows, vecs, p.tpr, (float)(vecs * 8), eps)
+  if (p.tpr == kWave) {
+    if (exact) BLOOM_LN_FWD(true, true, 1); else BLOOM_LN_FWD(true, false, 1);
+  } else if (exact && NV == 7 && MAXB == 256) {
+    BLOOM_LN_FWD(false, true, 5);
+  } else {
+    if (exact) BLOOM_LN_FWD(false, true, 1); else BLOOM_LN_FWD(false, false, 1);
+  }
+#undef BLOOM_LN_FWD
 }
 
 template <int NV, int MAXB, bool RES>
