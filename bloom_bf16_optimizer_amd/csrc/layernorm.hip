@@ -56,9 +56,12 @@ __device__ __forceinline__ uint4 add_bf16x8(const uint4& a, const uint4& b) {
 // its own reduction and index arithmetic.  WPE: the waves per SIMD the
 // register allocation must allow (1: no constraint).  At H = 14336 (256 x 7)
 // the block-team kernel fits 95 VGPRs with WPE = 5, five one-row workgroups
-// per compute unit instead of four: [2048, 14336] 23.8-24.4 -> 22.7-22.9 us
-// in one process; at [8192, 14336] the two are within run-to-run spread
-// (84.1-85.2 us either way).
+// per compute unit instead of four.  That wins while the whole launch is
+// short and loses on long ones (same process, outputs bit-identical, against
+// the four-wave kernel without the exact cover): [2048, 14336] 22.5 against
+// 23.8 us, [2560] 30.8 against 29.5, [3072] 34.0 against 34.0, [4096] 44.0
+// against 43.5, [8192] 83.9 against 82.6.  So the five-wave kernel runs when
+// the rows fit in two rounds of four one-row workgroups per compute unit.
 template <int NV, int MAXB, bool RES, bool WAVE, bool EXACT, int WPE>
 __global__ __launch_bounds__(MAXB) __attribute__((amdgpu_waves_per_eu(WPE)))
 void ln_fwd_kernel(
@@ -570,13 +573,16 @@ void launch_fwd(const RowPlan& p, hipStream_t s, const uint4* x, const uint4* re
                 const uint4* g, const uint4* b, uint4* y, float* mean, float* rstd, int64_t rows,
                 int vecs, float eps) {
   const bool exact = p.tpr * NV == vecs && (p.tpr == kWave || p.tpr == MAXB);
+  const bool short_launch = rows <= (int64_t)8 * device_cu_count();
 #define BLOOM_LN_FWD(WAVE, EXACT, WPE)                                                                          \
   hipLaunchKernelGGL((ln_fwd_kernel<NV, MAXB, RES, WAVE, EXACT, WPE>), dim3(p.grid), dim3(p.block), 0, s, x, res, h, \
                      g, b, y, mean, rstd, rows, vecs, p.tpr, (float)(vecs * 8), eps)
   if (p.tpr == kWave) {
     if (exact) BLOOM_LN_FWD(true, true, 1); else BLOOM_LN_FWD(true, false, 1);
-  } else if (exact && NV == 7 && MAXB == 256) {
+  } else if (exact && NV == 7 && MAXB == 256 && short_launch) {
     BLOOM_LN_FWD(false, true, 5);
+  } else if (NV == 7 && MAXB == 256) {
+    BLOOM_LN_FWD(false, false, 1);
   } else {
     if (exact) BLOOM_LN_FWD(false, true, 1); else BLOOM_LN_FWD(false, false, 1);
   }
