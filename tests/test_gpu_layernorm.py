@@ -103,6 +103,23 @@ def test_embedding_layernorm_long_context_sampled():
     assert np.allclose(tr.cpu().numpy()[sel], rr, rtol=1e-5, atol=0)
 
 
+def test_layernorm_fwd_across_the_launch_switch():
+    """At H = 14336 the forward runs its five-workgroups-per-CU kernel while the
+    rows fit in two rounds of four per compute unit (rows <= 8 x CUs) and its
+    four-per-CU kernel above that.  Both sides of the switch, every element
+    against the oracle; the rows both launches share must come out bit-identical
+    (the same arithmetic in the same order)."""
+    require_gpu()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    hidden = 14336
+    x, g, b, _ = _inputs_host(14, 8 * cus + 1, hidden)
+    y_hi, _, r_hi = _run_fwd(x, g, b)
+    y_lo, _, r_lo = _run_fwd(x[:-1], g, b)
+    assert np.array_equal(y_hi[:-1], y_lo) and np.array_equal(r_hi[:-1], r_lo)
+    _check_fwd(f"switch {8 * cus + 1}x{hidden}", x, g, b)
+    _check_fwd(f"switch {8 * cus}x{hidden}", x[:-1], g, b)
+
+
 # (600, 8192), (777, 5120) and (300, 12288) take the streaming backward with
 # 2-4 rows per workgroup (counts differ between workgroups); (7, 16384) with one;
 # (600, 2048) and (777, 2048) its four-wave team at H = 2048 with two
