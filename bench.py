@@ -193,8 +193,8 @@ def measured_traffic(kernel_key):
 # The CPU oracle, timed on the host's cores.
 def cpu_share():
     """Cores the oracle may use: the process's CPU affinity, capped by the
-    thread allotment OMP_NUM_THREADS states (the GPU machines allot 16 CPUs to a
-    one-GPU job and set it to 16)."""
+    thread allotment OMP_NUM_THREADS states (a job scheduler that shares a
+    host between GPUs sets it to the job's CPU share)."""
     try:
         aff = len(os.sched_getaffinity(0))
     except AttributeError:
