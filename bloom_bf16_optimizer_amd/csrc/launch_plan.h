@@ -26,14 +26,15 @@ inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // Team width for a row of `vecs` vectors with at most nv_cap vectors per
 // thread: as few idle lanes as possible, and among equally good widths the
 // widest team (fewest vectors per thread: lower register use, more waves in
-// flight per compute unit).
+// flight per compute unit).  A row too wide for the cap even at 1024 threads
+// gets the widest team with as few vectors per thread as cover it.
 inline void pick_team(int vecs, int nv_cap, int& tpr, int& nv) {
   if (vecs <= 64 * nv_cap) {
     tpr = 64;
     nv = ceil_div(vecs, 64);
     return;
   }
-  int best_w = 16, best_waste = 1 << 30, best_nv = 8;
+  int best_w = 16, best_waste = 1 << 30, best_nv = ceil_div(vecs, 1024);
   for (int w = 16; w >= 2; --w) {
     const int t = 64 * w;
     const int n = ceil_div(vecs, t);
@@ -61,7 +62,7 @@ inline void pick_team_narrow(int vecs, int nv_cap, int& tpr, int& nv) {
     nv = ceil_div(vecs, 64);
     return;
   }
-  int best_w = 16, best_waste = 1 << 30, best_nv = nv_cap;
+  int best_w = 16, best_waste = 1 << 30, best_nv = ceil_div(vecs, 1024);
   for (int w = 2; w <= 16; ++w) {
     const int t = 64 * w;
     const int n = ceil_div(vecs, t);

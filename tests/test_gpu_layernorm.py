@@ -123,10 +123,12 @@ def test_layernorm_fwd_across_the_launch_switch():
 # (600, 8192), (777, 5120) and (300, 12288) take the streaming backward with
 # 2-4 rows per workgroup (counts differ between workgroups); (7, 16384) with one;
 # (600, 2048) and (777, 2048) its four-wave team at H = 2048 with two
-# workgroups per compute unit, where some workgroups get 1 row and others 2.
+# workgroups per compute unit, where some workgroups get 1 row and others 2;
+# (3, 40000) and (2, 49152) the 1024-thread backward team with 5 and 6
+# vectors per thread (rows wider than 4 vectors per thread at 1024 threads).
 @pytest.mark.parametrize("rows,hidden", [(1, 8), (3, 1000), (5, 4104), (7, 16384), (33, 2056), (2, 65536),
                                          (130, 64), (9, 4096), (4, 4112), (600, 8192), (777, 5120),
-                                         (300, 12288), (600, 2048), (777, 2048)])
+                                         (300, 12288), (600, 2048), (777, 2048), (3, 40000), (2, 49152)])
 def test_layernorm_ragged_shapes(rows, hidden):
     require_gpu()
     x, g, b, dy = _inputs_host(11, rows, hidden)

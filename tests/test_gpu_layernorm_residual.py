@@ -86,7 +86,7 @@ def test_layernorm_residual_workloads_full(wl):
 # block and wave teams; (600, 2048), (777, 2048): the four-wave team at
 # H = 2048, two workgroups per compute unit, 1 or 2 rows per workgroup.
 @pytest.mark.parametrize("rows,hidden", [(600, 8192), (777, 5120), (7, 16384), (5, 4104), (3, 1000), (1, 8),
-                                         (2, 65536), (600, 2048), (777, 2048)])
+                                         (2, 65536), (600, 2048), (777, 2048), (3, 40000)])
 def test_layernorm_residual_ragged(rows, hidden):
     require_gpu()
     _check(f"ragged {rows}x{hidden}", *_inputs(21, rows, hidden))
