@@ -8,10 +8,13 @@
 //   z_ij = scale*(q_i . k_j) - slope_h*(i - j) for j <= i (else masked),
 //   o_i  = sum_j softmax_j(z_i) v_j,   lse_i = log sum_j exp(z_ij).
 //
-// Layout and mapping.  q, k, v, o are [B, NH, L, D] bf16 (D = 32, 64 or 128);
-// a workgroup of four waves takes 128 consecutive queries of one (b, h), a
-// wave 32 of them.  Keys are streamed in blocks of 64: K row-major and V
-// transposed (V^T[d][key]) are staged in LDS, padded by 16 bytes per row.
+// Layout and mapping.  q, k, v, o are [B, NH, L, D] bf16 (D = 32, 64 or 128).
+// An item is 128 consecutive queries of one (b, h); a workgroup of eight
+// waves (two key streams of four, a wave per 32 queries in each) works
+// through a fixed list of items, one workgroup per compute unit, and starts
+// the next item's Q and first key blocks while it merges and stores the
+// current one.  Keys are streamed in blocks of 64 through unpadded,
+// XOR-swizzled row-major K and V tiles in LDS (V read transposed).
 // Matrix products use v_mfma_f32_32x32x16_bf16 (A 32x16, B 16x32, FP32
 // accumulate; lane l supplies row/column l%32 and k-half l/32).  Scores are
 // formed transposed, S^T = K Q^T, so that lane l owns query l%32: its scores
@@ -204,161 +207,207 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     bool xcd_split, float scale2, AttnSlopes slopes) {
   constexpr int KS = D / 16;            // MFMA k-steps over the head dimension
   constexpr int DT = D / 32;            // 32-wide tiles of the head dimension
-  constexpr int VPR = D / 8;            // 16-byte vectors per K/V row
   constexpr int CH = AttnTile<D>::CHUNKS;
   // [stage][stream][K, V] tiles: the next pair of key blocks arrives while
-  // this pair is used.  At the end the same memory carries stream 1's
-  // partial results to stream 0.
+  // this pair is used.  At the end of an item the same memory carries stream
+  // 1's partial results to stream 0.
   __shared__ __attribute__((aligned(16))) uint4 tiles[2][2][2][CH];
   static_assert(sizeof(tiles) >= 4 * (DT * 16 + 2) * kWave * sizeof(float), "merge area");
 
-  // Two streams of four waves take the same 128 queries (wave w and w+4 the
-  // same 32) and alternate over the key blocks, so a workgroup's serial
-  // chain is half its key blocks; their partial softmax states merge at the
-  // end.
   const int t = threadIdx.x;
   const int w = t / kWave, lane = t & (kWave - 1), half = lane >> 5, col = lane & 31;
   const int stream = w >> 2, wq = w & 3;
-  // Causal work grows with the query block, so the longest workgroups are
-  // dispatched first and the short ones fill the tail.  Workgroup i runs on
-  // XCD i % 8, and each XCD has its own L2: with xcd_split, every (b, h) is
-  // cut into its even and odd query blocks, XCD x takes half-heads
-  // [x*n, (x+1)*n) and walks them heaviest query block first, so an XCD's L2
-  // holds the K and V of at most n/2 + 1 heads.  Otherwise the grid walks
-  // query blocks from the last to the first, every (b, h) at each step.
-  int qb;
-  int64_t bh;
-  if (xcd_split) {
-    const int x = (int)(blockIdx.x % 8u), j = (int)(blockIdx.x / 8u);
-    const int n = bh_count / 4;  // half-heads per XCD
-    const int rank = j / n, hh = n * x + j % n, par = hh & 1;
-    bh = hh >> 1;
-    qb = qblocks - 1 - ((qblocks - 1 - par) & 1) - 2 * rank;
-  } else {
-    qb = qblocks - 1 - (int)(blockIdx.x / (unsigned)bh_count);
-    bh = blockIdx.x % (unsigned)bh_count;
-  }
-  const int h = (int)(bh % heads);
-  const float slope2 = slopes.s[h];
-  const int64_t base = bh * (int64_t)seq;  // row index of (b, h, 0)
-  const int q0 = qb * kAttnBlockM + wq * 32;  // this wave's first query
-  const int qi = q0 + col;                    // this lane's query
-  const bool qvalid = qi < seq;
-  const bool wave_live = q0 < seq;
+  attn_lds_uint4* lt = (attn_lds_uint4*)&tiles[0][0][0][0];
+  auto tile = [&](int stage, int which) { return lt + ((stage * 2 + stream) * 2 + which) * CH; };
 
-  // Q^T operand fragments: lane supplies q[qi][16*kk + 8*half .. +8].
-  bf16x8_t qf[KS];
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    const uint4 u = qvalid ? q[(base + qi) * VPR + 2 * kk + half] : make_uint4(0u, 0u, 0u, 0u);
-    qf[kk] = as_bf16x8(u);
-  }
-  // ALiBi offset fragments: k-slots 0..2 of the lower lane half carry the key
-  // offset in the block (an integer < 64, exact in bf16) against slope/scale
-  // split into three bf16 parts; every other slot is zero.
-  bf16x8_t kx[2], qx;
+  // ALiBi key-offset fragments (the same for every item): k-slots 0..2 of
+  // the lower lane half carry the key offset in the block.
+  bf16x8_t kx[2];
   {
-    const float cs = slope2 / scale2;  // slope/scale
-    const __bf16 c1 = (__bf16)cs;
-    const float r1 = cs - (float)c1;
-    const __bf16 c2 = (__bf16)r1;
-    const __bf16 c3 = (__bf16)(r1 - (float)c2);
     const __bf16 z = (__bf16)0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const bool on = half == 0 && j < 3;
-      qx[j] = on ? (j == 0 ? c1 : (j == 1 ? c2 : c3)) : z;
       kx[0][j] = on ? (__bf16)(float)col : z;
       kx[1][j] = on ? (__bf16)(float)(col + 32) : z;
     }
   }
 
-  AttnState<D> st;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) st.oacc[dt][i] = 0.f;
-  st.m = -INFINITY;
-  st.l = 0.f;
-
-  // Key blocks run from the diagonal back to key 0 (stream s takes blocks
-  // nkb-1-s, nkb-3-s, ...): the block holding a row's own key comes first,
-  // and with the ALiBi bias falling off with distance the running max then
-  // rarely moves.
-  const int wg_last_q = min(seq, (qb + 1) * kAttnBlockM) - 1;
-  const int nkb = wg_last_q / kAttnBlockN + 1;
-  const int iters = (nkb + 1) / 2;
-  attn_lds_uint4* lt = (attn_lds_uint4*)&tiles[0][0][0][0];
-  auto tile = [&](int stage, int which) { return lt + ((stage * 2 + stream) * 2 + which) * CH; };
-  int kb = nkb - 1 - stream;
-  if (kb >= 0) {
-    attn_request<D, false>(k, tile(0, 0), base, kb * kAttnBlockN, seq, wq, lane);
-    attn_request<D, true>(v, tile(0, 1), base, kb * kAttnBlockN, seq, wq, lane);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int it = 0, buf = 0; it < iters; ++it, buf ^= 1, kb -= 2) {
-    const int k0 = kb * kAttnBlockN;
-    // the next block's transfers run during this block's products (the
-    // barrier that ended the previous iteration freed their buffer)
-    if (kb >= 2) {
-      attn_request<D, false>(k, tile(buf ^ 1, 0), base, k0 - 2 * kAttnBlockN, seq, wq, lane);
-      attn_request<D, true>(v, tile(buf ^ 1, 1), base, k0 - 2 * kAttnBlockN, seq, wq, lane);
+  // Persistent workgroups: the grid is a multiple of 8 and workgroup g runs
+  // on XCD g % 8.  Items (one 128-query block of one (b, h)) are numbered so
+  // that item j belongs to XCD j % 8 and, within an XCD, heaviest first; the
+  // U workgroups of an XCD take its items in a snake (round r: local item
+  // r*U + u for even r, r*U + U-1-u for odd r), which pairs heavy with light
+  // items.
+  const int U = (int)(gridDim.x / 8u), x8 = (int)(blockIdx.x % 8u), u = (int)(blockIdx.x / 8u);
+  const int n_items = qblocks * bh_count;
+  // Item of round r of this workgroup: its (b, h) and query block, or none.
+  struct Item {
+    bool ok;
+    int qb;
+    int64_t bh;
+  };
+  auto item_of = [&](int r) {
+    Item it;
+    const int i_loc = r * U + ((r & 1) ? U - 1 - u : u);
+    const int j = i_loc * 8 + x8;
+    it.ok = j < n_items;
+    // Causal work grows with the query block.  With xcd_split every (b, h)
+    // is cut into its even and odd query blocks and XCD x takes half-heads
+    // [x*n, (x+1)*n), heaviest query block first, so an XCD's L2 holds the K
+    // and V of at most n/2 + 1 heads.  Otherwise items walk query blocks from
+    // the last to the first, every (b, h) at each step.
+    if (xcd_split) {
+      const int jj = j / 8;
+      const int n = bh_count / 4;  // half-heads per XCD
+      const int rank = jj / n, hh = n * x8 + jj % n, par = hh & 1;
+      it.bh = hh >> 1;
+      it.qb = qblocks - 1 - ((qblocks - 1 - par) & 1) - 2 * rank;
+    } else {
+      it.qb = qblocks - 1 - j / bh_count;
+      it.bh = j % bh_count;
     }
-    // Every processed block has k0 <= q0 (both are multiples of 32), so each
-    // row has its key k0 unmasked and the first block sets a finite max.
-    if (kb >= 0 && wave_live && k0 <= q0 + 31) {
-      if (k0 + kAttnBlockN - 1 > q0)
-        attn_block<D, true>(st, tile(buf, 0), tile(buf, 1), qf, kx, qx, scale2, slope2, k0, qi, half, col, lane);
-      else
-        attn_block<D, false>(st, tile(buf, 0), tile(buf, 1), qf, kx, qx, scale2, slope2, k0, qi, half, col, lane);
+    return it;
+  };
+  // Q^T operand fragments of an item: lane supplies q[qi][16*kk + 8*half .. +8].
+  bf16x8_t qf[KS];
+  auto load_q = [&](const Item& it) {
+    const int qi_ = it.qb * kAttnBlockM + wq * 32 + col;
+    const bool ok = qi_ < seq;
+    const int64_t row = it.bh * (int64_t)seq + qi_;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint4 uq = ok ? q[row * (D / 8) + 2 * kk + half] : make_uint4(0u, 0u, 0u, 0u);
+      qf[kk] = as_bf16x8(uq);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
+  };
+  // The first key block of an item for this stream (none if the item has
+  // fewer blocks than streams), into stage 0.
+  auto request_first = [&](const Item& it) {
+    const int nkb_ = (min(seq, (it.qb + 1) * kAttnBlockM) - 1) / kAttnBlockN + 1;
+    const int kb_ = nkb_ - 1 - stream;
+    if (kb_ >= 0) {
+      const int64_t base_ = it.bh * (int64_t)seq;
+      attn_request<D, false>(k, tile(0, 0), base_, kb_ * kAttnBlockN, seq, wq, lane);
+      attn_request<D, true>(v, tile(0, 1), base_, kb_ * kAttnBlockN, seq, wq, lane);
+    }
+  };
 
-  // Merge stream 1 into stream 0 through LDS ([wave][value][lane] floats).
-  // Block 0 is processed by one of the streams for every live row, so at
-  // least one of the two maxima is finite.
-  float* mg = reinterpret_cast<float*>(&tiles[0][0][0][0]) + wq * (DT * 16 + 2) * kWave + lane;
-  if (stream == 1) {
+  Item cur = item_of(0);
+  if (!cur.ok) return;  // uniform over the workgroup
+  load_q(cur);
+  request_first(cur);
+  for (int r = 0;; ++r) {
+    const int qb = cur.qb;
+    const int64_t bh = cur.bh;
+    const int h = (int)(bh % heads);
+    const float slope2 = slopes.s[h];
+    const int64_t base = bh * (int64_t)seq;  // row index of (b, h, 0)
+    const int q0 = qb * kAttnBlockM + wq * 32;  // this wave's first query
+    const int qi = q0 + col;                    // this lane's query
+    const bool qvalid = qi < seq;
+    const bool wave_live = q0 < seq;
+    // slope/scale split into three bf16 parts against the key offsets of kx
+    bf16x8_t qx;
+    {
+      const float cs = slope2 / scale2;
+      const __bf16 c1 = (__bf16)cs;
+      const float r1 = cs - (float)c1;
+      const __bf16 c2 = (__bf16)r1;
+      const __bf16 c3 = (__bf16)(r1 - (float)c2);
+      const __bf16 z = (__bf16)0.0f;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mg[(dt * 16 + i) * kWave] = st.oacc[dt][i];
-    mg[(DT * 16) * kWave] = st.m;
-    mg[(DT * 16 + 1) * kWave] = st.l;
-  }
-  __syncthreads();
-  if (stream == 1) return;
-  {
-    const float m1 = mg[(DT * 16) * kWave], l1 = mg[(DT * 16 + 1) * kWave];
-    const float m = fmaxf(st.m, m1);
-    const float a0 = __builtin_amdgcn_exp2f(st.m - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st.oacc[dt][i] = fmaf(st.oacc[dt][i], a0, mg[(dt * 16 + i) * kWave] * a1);
-    st.l = fmaf(st.l, a0, l1 * a1);
-    st.m = m;
-  }
-
-  // Normalise: the two lane halves hold the sums over complementary keys.
-  const float l_tot = st.l + __shfl_xor(st.l, 32, kWave);
-  const float inv = 1.0f / l_tot;
-  if (qvalid) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // d = 32*dt + 8*g + 4*half + 0..3
-        const uint32_t lo = pack2(st.oacc[dt][4 * g] * inv, st.oacc[dt][4 * g + 1] * inv);
-        const uint32_t hi = pack2(st.oacc[dt][4 * g + 2] * inv, st.oacc[dt][4 * g + 3] * inv);
-        o[(base + qi) * (D / 4) + (32 * dt + 8 * g + 4 * half) / 4] = make_uint2(lo, hi);
+      for (int jx = 0; jx < 8; ++jx) {
+        const bool on = half == 0 && jx < 3;
+        qx[jx] = on ? (jx == 0 ? c1 : (jx == 1 ? c2 : c3)) : z;
       }
     }
-    if (half == 0) lse[base + qi] = (st.m + __log2f(l_tot)) * 0.69314718055994530942f;
+
+    AttnState<D> st;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.oacc[dt][i] = 0.f;
+    st.m = -INFINITY;
+    st.l = 0.f;
+
+    // Key blocks run from the diagonal back to key 0 (stream s takes blocks
+    // nkb-1-s, nkb-3-s, ...); the first ones were requested already.
+    const int wg_last_q = min(seq, (qb + 1) * kAttnBlockM) - 1;
+    const int nkb = wg_last_q / kAttnBlockN + 1;
+    const int iters = (nkb + 1) / 2;
+    int kb = nkb - 1 - stream;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int it = 0, buf = 0; it < iters; ++it, buf ^= 1, kb -= 2) {
+      const int k0 = kb * kAttnBlockN;
+      if (kb >= 2) {
+        attn_request<D, false>(k, tile(buf ^ 1, 0), base, k0 - 2 * kAttnBlockN, seq, wq, lane);
+        attn_request<D, true>(v, tile(buf ^ 1, 1), base, k0 - 2 * kAttnBlockN, seq, wq, lane);
+      }
+      if (kb >= 0 && wave_live && k0 <= q0 + 31) {
+        if (k0 + kAttnBlockN - 1 > q0)
+          attn_block<D, true>(st, tile(buf, 0), tile(buf, 1), qf, kx, qx, scale2, slope2, k0, qi, half, col, lane);
+        else
+          attn_block<D, false>(st, tile(buf, 0), tile(buf, 1), qf, kx, qx, scale2, slope2, k0, qi, half, col, lane);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+
+    // The next item's Q arrives during the merge (this item's Q is done).
+    const Item nxt = item_of(r + 1);
+    if (nxt.ok) load_q(nxt);
+
+    // Merge stream 1 into stream 0 through LDS ([wave][value][lane] floats).
+    float* mg = reinterpret_cast<float*>(&tiles[0][0][0][0]) + wq * (DT * 16 + 2) * kWave + lane;
+    if (stream == 1) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mg[(dt * 16 + i) * kWave] = st.oacc[dt][i];
+      mg[(DT * 16) * kWave] = st.m;
+      mg[(DT * 16 + 1) * kWave] = st.l;
+    }
+    __syncthreads();
+    if (stream == 0) {
+      const float m1 = mg[(DT * 16) * kWave], l1 = mg[(DT * 16 + 1) * kWave];
+      const float m = fmaxf(st.m, m1);
+      const float a0 = __builtin_amdgcn_exp2f(st.m - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.oacc[dt][i] = fmaf(st.oacc[dt][i], a0, mg[(dt * 16 + i) * kWave] * a1);
+      st.l = fmaf(st.l, a0, l1 * a1);
+      st.m = m;
+    }
+    // The merge area is the next item's tile memory: every read of it ends
+    // here, and the next item's first key blocks are requested right after.
+    __syncthreads();
+    if (nxt.ok) request_first(nxt);
+    if (stream == 0) {
+      // Normalise: the two lane halves hold the sums over complementary keys.
+      const float l_tot = st.l + __shfl_xor(st.l, 32, kWave);
+      const float inv = 1.0f / l_tot;
+      if (qvalid) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            // d = 32*dt + 8*g + 4*half + 0..3
+            const uint32_t lo = pack2(st.oacc[dt][4 * g] * inv, st.oacc[dt][4 * g + 1] * inv);
+            const uint32_t hi = pack2(st.oacc[dt][4 * g + 2] * inv, st.oacc[dt][4 * g + 3] * inv);
+            o[(base + qi) * (D / 4) + (32 * dt + 8 * g + 4 * half) / 4] = make_uint2(lo, hi);
+          }
+        }
+        if (half == 0) lse[base + qi] = (st.m + __log2f(l_tot)) * 0.69314718055994530942f;
+      }
+    }
+    if (!nxt.ok) break;  // uniform over the workgroup
+    cur = nxt;
   }
+  // The last transfers issued (none after the final item) have landed: the
+  // loop's waits covered every request.
 }
 
 bloom_status check_attention(int64_t batch, int32_t heads, int64_t seq, int32_t head_dim) {
@@ -403,7 +452,10 @@ extern "C" bloom_status bloom_alibi_attention_fwd(const bloom_bf16* q, const blo
   for (int hh = 0; hh < BLOOM_MAX_HEADS; ++hh) table.s[hh] = (hh < heads) ? (float)((double)sl[hh] * log2e) : 0.f;
   const float scale2 = (float)((double)scale * log2e);
   const int qblocks = (int)((seq + kAttnBlockM - 1) / kAttnBlockM);
-  const dim3 grid((unsigned)(batch * heads * qblocks));
+  const int64_t n_items = batch * heads * qblocks;
+  const int64_t cu8 = (int64_t)(device_cu_count() / 8) * 8;
+  const int64_t g8 = (n_items + 7) / 8 * 8;
+  const dim3 grid((unsigned)(g8 < cu8 ? g8 : (cu8 > 0 ? cu8 : 8)));
   // whole half-heads per XCD: an even number of query blocks, (b, h) pairs a multiple of 4
   const bool xcd_split = qblocks % 2 == 0 && (batch * heads) % 4 == 0;
   const uint4* qv = reinterpret_cast<const uint4*>(q);
