@@ -186,90 +186,126 @@ __global__ __launch_bounds__(kBwdThreads) void attention_bwd_dq_kernel(
 
   const int t = threadIdx.x;
   const int w = t / kWave, lane = t & (kWave - 1), half = lane >> 5, col = lane & 31;
-  // the longest workgroups (last query blocks) first
-  const int qb = qblocks - 1 - (int)(blockIdx.x / (unsigned)bh_count);
-  const int64_t bh = blockIdx.x % (unsigned)bh_count;
-  const int h = (int)(bh % heads);
-  const float slope2 = slopes.s[h];
-  const int64_t base = bh * (int64_t)seq;
-  const int q0 = qb * kBwdBlock + w * 32;
-  const int qi = q0 + col;
-  const bool qvalid = qi < seq;
-  const bool wave_live = q0 < seq;
-
-  // B operands: this lane's query row of q and dO (d = 16*kk + 8*half .. +8)
-  bf16x8_t qf[KS], df[KS];
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
-    const int64_t idx = (base + qi) * VPR + 2 * kk + half;
-    qf[kk] = as_bf16x8(qvalid ? q[idx] : z4);
-    df[kk] = as_bf16x8(qvalid ? dout[idx] : z4);
-  }
-  const float lse2 = qvalid ? lse[base + qi] * kLog2e : 0.f;
-
-  f32x16_t acc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
-
-  const int wg_last_q = min(seq, (qb + 1) * kBwdBlock) - 1;
-  const int nkb = wg_last_q / kBwdRows + 1;  // key blocks nkb-1 .. 0, streamed once per pass
   attn_lds_uint4* lt = (attn_lds_uint4*)&tiles[0][0][0];
   auto tile = [&](int stage, int which) { return lt + (stage * 2 + which) * CH; };
-  float dsum = 0.f, delta = 0.f;
-  for (int pass = 0; pass < 2; ++pass) {
-    int kb = nkb - 1;
-    bwd_request<D>(k, tile(0, 0), base, kb * kBwdRows, seq, w, lane);
-    bwd_request<D>(v, tile(0, 1), base, kb * kBwdRows, seq, w, lane);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    for (int buf = 0; kb >= 0; --kb, buf ^= 1) {
-      const int k0 = kb * kBwdRows;
-      // the next block arrives while this one is used (the barrier that ended
-      // the previous iteration freed its buffer)
-      if (kb >= 1) {
-        bwd_request<D>(k, tile(buf ^ 1, 0), base, k0 - kBwdRows, seq, w, lane);
-        bwd_request<D>(v, tile(buf ^ 1, 1), base, k0 - kBwdRows, seq, w, lane);
-      }
-      if (wave_live && k0 <= q0 + 31) {
-        const bool diag = k0 + kBwdRows - 1 > q0;
-        if (pass == 0) {
-          if (diag)
-            dq_block<D, true, true>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta, k0,
-                                    qi, half, col, lane);
-          else
-            dq_block<D, false, true>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta, k0,
-                                     qi, half, col, lane);
-        } else {
-          if (diag)
-            dq_block<D, true, false>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta, k0,
-                                     qi, half, col, lane);
-          else
-            dq_block<D, false, false>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta,
-                                      k0, qi, half, col, lane);
-        }
-      }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+
+  // Persistent workgroups: a workgroup takes items (128 queries of one (b, h),
+  // numbered longest first: item j is query block qblocks-1-j/bh_count of
+  // (b, h) = j % bh_count) in a snake over the grid (round r: item r*G + g
+  // for even r, r*G + G-1-g for odd r), so heavy items pair with light ones.
+  // While an item's last key block is used, the next stage's first block is
+  // already on its way: the second pass's during the first pass, the next
+  // item's during the second, with the next item's q and dO rows loaded
+  // before this item's dq is stored.
+  const int G = (int)gridDim.x, g = (int)blockIdx.x;
+  const int n_items = qblocks * bh_count;
+  auto item_j = [&](int r) { return r * G + ((r & 1) ? G - 1 - g : g); };
+  auto nkb_of = [&](int qb_) { return (min(seq, (qb_ + 1) * kBwdBlock) - 1) / kBwdRows + 1; };
+
+  int j = item_j(0);
+  if (j >= n_items) return;  // uniform over the workgroup
+  // B operands: this lane's query row of q and dO (d = 16*kk + 8*half .. +8)
+  bf16x8_t qf[KS], df[KS];
+  float lse2;
+  auto load_rows = [&](int jn) {
+    const int qb_ = qblocks - 1 - jn / bh_count;
+    const int64_t bh_ = jn % bh_count;
+    const int qi_ = qb_ * kBwdBlock + w * 32 + col;
+    const bool ok = qi_ < seq;
+    const int64_t row = bh_ * (int64_t)seq + qi_;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+      const int64_t idx = row * VPR + 2 * kk + half;
+      qf[kk] = as_bf16x8(ok ? q[idx] : z4);
+      df[kk] = as_bf16x8(ok ? dout[idx] : z4);
     }
-    if (pass == 0) {
-      // the two lane halves summed complementary keys of the same query
-      delta = dsum + __shfl_xor(dsum, 32, kWave);
-      if (qvalid && half == 0) delta_out[base + qi] = delta;
-    }
-  }
-  if (qvalid) {
+    lse2 = ok ? lse[row] * kLog2e : 0.f;
+  };
+  auto request_block = [&](int jn, int kb_, int stage) {
+    const int64_t base_ = (int64_t)(jn % bh_count) * seq;
+    bwd_request<D>(k, tile(stage, 0), base_, kb_ * kBwdRows, seq, w, lane);
+    bwd_request<D>(v, tile(stage, 1), base_, kb_ * kBwdRows, seq, w, lane);
+  };
+  load_rows(j);
+  request_block(j, nkb_of(qblocks - 1 - j / bh_count) - 1, 0);
+  int buf = 0;  // the stage holding the next block to use
+  for (int r = 0;; ++r) {
+    const int qb = qblocks - 1 - j / bh_count;
+    const int64_t bh = j % bh_count;
+    const int h = (int)(bh % heads);
+    const float slope2 = slopes.s[h];
+    const int64_t base = bh * (int64_t)seq;
+    const int q0 = qb * kBwdBlock + w * 32;
+    const int qi = q0 + col;
+    const bool qvalid = qi < seq;
+    const bool wave_live = q0 < seq;
+    const int jn = item_j(r + 1);
+    const bool has_next = jn < n_items;
+
+    f32x16_t acc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // d = 32*dt + 8*g + 4*half + 0..3
-        const uint32_t lo = pack2(acc[dt][4 * g] * scale, acc[dt][4 * g + 1] * scale);
-        const uint32_t hi = pack2(acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale);
-        dq[(base + qi) * (D / 4) + (32 * dt + 8 * g + 4 * half) / 4] = make_uint2(lo, hi);
+      for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+
+    const int nkb = nkb_of(qb);  // key blocks nkb-1 .. 0, streamed once per pass
+    float dsum = 0.f, delta = 0.f;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int kb = nkb - 1; kb >= 0; --kb, buf ^= 1) {
+        const int k0 = kb * kBwdRows;
+        // the next block arrives while this one is used (the barrier that
+        // ended the previous iteration freed its buffer)
+        if (kb >= 1)
+          request_block(j, kb - 1, buf ^ 1);
+        else if (pass == 0)
+          request_block(j, nkb - 1, buf ^ 1);
+        else if (has_next)
+          request_block(jn, nkb_of(qblocks - 1 - jn / bh_count) - 1, buf ^ 1);
+        if (wave_live && k0 <= q0 + 31) {
+          const bool diag = k0 + kBwdRows - 1 > q0;
+          if (pass == 0) {
+            if (diag)
+              dq_block<D, true, true>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta, k0,
+                                      qi, half, col, lane);
+            else
+              dq_block<D, false, true>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta,
+                                       k0, qi, half, col, lane);
+          } else {
+            if (diag)
+              dq_block<D, true, false>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta,
+                                       k0, qi, half, col, lane);
+            else
+              dq_block<D, false, false>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta,
+                                        k0, qi, half, col, lane);
+          }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
       }
+      if (pass == 0) {
+        // the two lane halves summed complementary keys of the same query
+        delta = dsum + __shfl_xor(dsum, 32, kWave);
+        if (qvalid && half == 0) delta_out[base + qi] = delta;
+      }
+    }
+    // this item's q, dO and lse are no longer needed: the next item's load now
+    if (has_next) load_rows(jn);
+    if (qvalid) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          // d = 32*dt + 8*gg + 4*half + 0..3
+          const uint32_t lo = pack2(acc[dt][4 * gg] * scale, acc[dt][4 * gg + 1] * scale);
+          const uint32_t hi = pack2(acc[dt][4 * gg + 2] * scale, acc[dt][4 * gg + 3] * scale);
+          dq[(base + qi) * (D / 4) + (32 * dt + 8 * gg + 4 * half) / 4] = make_uint2(lo, hi);
+        }
+    }
+    if (!has_next) break;  // uniform over the workgroup
+    j = jn;
   }
 }
 
@@ -452,11 +488,15 @@ void launch_bwd(const bloom_bf16* q, const bloom_bf16* k, const bloom_bf16* v, c
   const int bh_count = (int)(batch * heads);
   const int blocks = (int)((seq + kBwdBlock - 1) / kBwdBlock);
   const dim3 grid((unsigned)(bh_count * blocks));
+  // the dq kernel is persistent: one workgroup per compute unit, at most one per item
+  const int64_t n_items = (int64_t)bh_count * blocks;
+  const int cus = device_cu_count();
+  const dim3 grid_dq((unsigned)(n_items < cus ? n_items : (cus > 0 ? cus : 1)));
   const uint4* qv = reinterpret_cast<const uint4*>(q);
   const uint4* kv = reinterpret_cast<const uint4*>(k);
   const uint4* vv = reinterpret_cast<const uint4*>(v);
   const uint4* dov = reinterpret_cast<const uint4*>(dout);
-  hipLaunchKernelGGL((attention_bwd_dq_kernel<D>), grid, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov, lse,
+  hipLaunchKernelGGL((attention_bwd_dq_kernel<D>), grid_dq, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov, lse,
                      reinterpret_cast<uint2*>(dq), delta, (int)seq, (int)heads, blocks, bh_count, scale2, scale,
                      table);
   hipLaunchKernelGGL((attention_bwd_dkdv_kernel<D>), grid, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov, lse,
