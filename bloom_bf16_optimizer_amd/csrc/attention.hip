@@ -410,6 +410,119 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   // loop's waits covered every request.
 }
 
+// The same forward with one key stream per workgroup: four waves take the
+// 128 queries of one item and walk all its key blocks from the diagonal back,
+// with no merge; a workgroup holds half the LDS and two share a compute unit.
+// Two independent workgroups per unit hide each other's start-up and
+// output stores, which wins when every unit gets many items (long
+// sequences); the two-stream kernel halves the longest item's chain, which
+// wins when the longest item is a large share of a unit's work.
+template <int D>
+__global__ __launch_bounds__(kAttnGroupThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_fwd_stream_kernel(
+    const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
+    uint2* __restrict__ o, float* __restrict__ lse, int seq, int heads, int qblocks, int bh_count,
+    bool xcd_split, float scale2, AttnSlopes slopes) {
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int VPR = D / 8;
+  constexpr int CH = AttnTile<D>::CHUNKS;
+  __shared__ __attribute__((aligned(16))) uint4 tiles[2][2][CH];  // [stage][K, V]
+
+  const int t = threadIdx.x;
+  const int w = t / kWave, lane = t & (kWave - 1), half = lane >> 5, col = lane & 31;
+  // Workgroup i runs on XCD i % 8; the items are mapped as in the two-stream
+  // kernel (each XCD takes a contiguous range of half-heads), heaviest first.
+  int qb;
+  int64_t bh;
+  if (xcd_split) {
+    const int x = (int)(blockIdx.x % 8u), j = (int)(blockIdx.x / 8u);
+    const int n = bh_count / 4;  // half-heads per XCD
+    const int rank = j / n, hh = n * x + j % n, par = hh & 1;
+    bh = hh >> 1;
+    qb = qblocks - 1 - ((qblocks - 1 - par) & 1) - 2 * rank;
+  } else {
+    qb = qblocks - 1 - (int)(blockIdx.x / (unsigned)bh_count);
+    bh = blockIdx.x % (unsigned)bh_count;
+  }
+  const int h = (int)(bh % heads);
+  const float slope2 = slopes.s[h];
+  const int64_t base = bh * (int64_t)seq;
+  const int q0 = qb * kAttnBlockM + w * 32;
+  const int qi = q0 + col;
+  const bool qvalid = qi < seq;
+  const bool wave_live = q0 < seq;
+
+  bf16x8_t qf[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    const uint4 u = qvalid ? q[(base + qi) * VPR + 2 * kk + half] : make_uint4(0u, 0u, 0u, 0u);
+    qf[kk] = as_bf16x8(u);
+  }
+  bf16x8_t kx[2], qx;
+  {
+    const float cs = slope2 / scale2;
+    const __bf16 c1 = (__bf16)cs;
+    const float r1 = cs - (float)c1;
+    const __bf16 c2 = (__bf16)r1;
+    const __bf16 c3 = (__bf16)(r1 - (float)c2);
+    const __bf16 z = (__bf16)0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool on = half == 0 && j < 3;
+      qx[j] = on ? (j == 0 ? c1 : (j == 1 ? c2 : c3)) : z;
+      kx[0][j] = on ? (__bf16)(float)col : z;
+      kx[1][j] = on ? (__bf16)(float)(col + 32) : z;
+    }
+  }
+
+  AttnState<D> st;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.oacc[dt][i] = 0.f;
+  st.m = -INFINITY;
+  st.l = 0.f;
+
+  const int wg_last_q = min(seq, (qb + 1) * kAttnBlockM) - 1;
+  const int nkb = wg_last_q / kAttnBlockN + 1;
+  attn_lds_uint4* lt = (attn_lds_uint4*)&tiles[0][0][0];
+  auto tile = [&](int stage, int which) { return lt + (stage * 2 + which) * CH; };
+  int kb = nkb - 1;
+  attn_request<D, false>(k, tile(0, 0), base, kb * kAttnBlockN, seq, w, lane);
+  attn_request<D, true>(v, tile(0, 1), base, kb * kAttnBlockN, seq, w, lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int buf = 0; kb >= 0; buf ^= 1, --kb) {
+    const int k0 = kb * kAttnBlockN;
+    if (kb >= 1) {
+      attn_request<D, false>(k, tile(buf ^ 1, 0), base, k0 - kAttnBlockN, seq, w, lane);
+      attn_request<D, true>(v, tile(buf ^ 1, 1), base, k0 - kAttnBlockN, seq, w, lane);
+    }
+    if (wave_live && k0 <= q0 + 31) {
+      if (k0 + kAttnBlockN - 1 > q0)
+        attn_block<D, true>(st, tile(buf, 0), tile(buf, 1), qf, kx, qx, scale2, slope2, k0, qi, half, col, lane);
+      else
+        attn_block<D, false>(st, tile(buf, 0), tile(buf, 1), qf, kx, qx, scale2, slope2, k0, qi, half, col, lane);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  const float l_tot = st.l + __shfl_xor(st.l, 32, kWave);
+  const float inv = 1.0f / l_tot;
+  if (qvalid) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t lo = pack2(st.oacc[dt][4 * g] * inv, st.oacc[dt][4 * g + 1] * inv);
+        const uint32_t hi = pack2(st.oacc[dt][4 * g + 2] * inv, st.oacc[dt][4 * g + 3] * inv);
+        o[(base + qi) * (D / 4) + (32 * dt + 8 * g + 4 * half) / 4] = make_uint2(lo, hi);
+      }
+    }
+    if (half == 0) lse[base + qi] = (st.m + __log2f(l_tot)) * 0.69314718055994530942f;
+  }
+}
+
 bloom_status check_attention(int64_t batch, int32_t heads, int64_t seq, int32_t head_dim) {
   BLOOM_REQUIRE(batch >= 0 && heads >= 0, BLOOM_ERR_SHAPE, "batch and heads must be >= 0");
   BLOOM_REQUIRE(heads <= BLOOM_MAX_HEADS, BLOOM_ERR_SHAPE, "heads = %d exceeds %d", heads, BLOOM_MAX_HEADS);
@@ -453,28 +566,49 @@ extern "C" bloom_status bloom_alibi_attention_fwd(const bloom_bf16* q, const blo
   const float scale2 = (float)((double)scale * log2e);
   const int qblocks = (int)((seq + kAttnBlockM - 1) / kAttnBlockM);
   const int64_t n_items = batch * heads * qblocks;
-  const int64_t cu8 = (int64_t)(device_cu_count() / 8) * 8;
+  const int cus = device_cu_count();
+  const int64_t cu8 = (int64_t)(cus / 8) * 8;
   const int64_t g8 = (n_items + 7) / 8 * 8;
   const dim3 grid((unsigned)(g8 < cu8 ? g8 : (cu8 > 0 ? cu8 : 8)));
+  // One key stream per workgroup, two workgroups per unit, when a unit's
+  // share of the key blocks is at least 1.5x the longest item's (the longest
+  // item is the last query block: all its key blocks).  Measured at
+  // [1,28,8192,128]: 472.6 against 535.0 us; at [1,28,2048,128]: 54.2 against
+  // 44.5 us, where the longest item is two thirds of a unit's share.
+  const int64_t nkb_max = (seq - 1) / kAttnBlockN + 1;
+  const int64_t blocks_total = (int64_t)batch * heads *
+                               [&] {
+                                 int64_t t = 0;
+                                 for (int qb = 0; qb < qblocks; ++qb)
+                                   t += (std::min<int64_t>(seq, (int64_t)(qb + 1) * kAttnBlockM) - 1) / kAttnBlockN + 1;
+                                 return t;
+                               }();
+  const bool one_stream = 2 * blocks_total >= 3 * nkb_max * 2 * (int64_t)(cus > 0 ? cus : 1);
   // whole half-heads per XCD: an even number of query blocks, (b, h) pairs a multiple of 4
   const bool xcd_split = qblocks % 2 == 0 && (batch * heads) % 4 == 0;
   const uint4* qv = reinterpret_cast<const uint4*>(q);
   const uint4* kv = reinterpret_cast<const uint4*>(k);
   const uint4* vv = reinterpret_cast<const uint4*>(v);
   uint2* ov = reinterpret_cast<uint2*>(o);
+  const dim3 grid1((unsigned)n_items);
+#define BLOOM_ATTN_FWD(DD)                                                                                        \
+  if (one_stream)                                                                                                 \
+    hipLaunchKernelGGL((attention_fwd_stream_kernel<DD>), grid1, dim3(kAttnGroupThreads), 0, stream, qv, kv, vv, \
+                       ov, lse, (int)seq, (int)heads, qblocks, (int)(batch * heads), xcd_split, scale2, table);    \
+  else                                                                                                            \
+    hipLaunchKernelGGL((attention_fwd_kernel<DD>), grid, dim3(kAttnThreads), 0, stream, qv, kv, vv, ov, lse,      \
+                       (int)seq, (int)heads, qblocks, (int)(batch * heads), xcd_split, scale2, table);
   switch (head_dim) {
     case 32:
-      hipLaunchKernelGGL((attention_fwd_kernel<32>), grid, dim3(kAttnThreads), 0, stream, qv, kv, vv, ov, lse,
-                         (int)seq, (int)heads, qblocks, (int)(batch * heads), xcd_split, scale2, table);
+      BLOOM_ATTN_FWD(32)
       break;
     case 64:
-      hipLaunchKernelGGL((attention_fwd_kernel<64>), grid, dim3(kAttnThreads), 0, stream, qv, kv, vv, ov, lse,
-                         (int)seq, (int)heads, qblocks, (int)(batch * heads), xcd_split, scale2, table);
+      BLOOM_ATTN_FWD(64)
       break;
     default:
-      hipLaunchKernelGGL((attention_fwd_kernel<128>), grid, dim3(kAttnThreads), 0, stream, qv, kv, vv, ov, lse,
-                         (int)seq, (int)heads, qblocks, (int)(batch * heads), xcd_split, scale2, table);
+      BLOOM_ATTN_FWD(128)
       break;
   }
+#undef BLOOM_ATTN_FWD
   return launch_status("bloom_alibi_attention_fwd");
 }
