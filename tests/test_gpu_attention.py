@@ -77,6 +77,29 @@ def test_attention_max_seq_16384_sampled():
     _check("max seq 16384", q, k, v, 0, 112, float(np.float32(1.0 / np.sqrt(128.0))), rows)
 
 
+def _one_stream(b, h, s):
+    """Whether the forward takes its one-stream-per-workgroup kernel on this
+    GPU: when a compute unit's share of the 64-key blocks (two workgroups per
+    unit) is at least 1.5x the longest item's, the last query block's."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    qblocks = (s + 127) // 128
+    total = b * h * sum((min(s, (qb + 1) * 128) - 1) // 64 + 1 for qb in range(qblocks))
+    return 2 * total >= 3 * ((s - 1) // 64 + 1) * 2 * cus
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("b,h,s,d,seed", [(1, 28, 8192, 128, 3), (1, 128, 2048, 32, 41), (1, 96, 2048, 64, 42)])
+def test_attention_one_stream_kernel_sampled(b, h, s, d, seed):
+    """Shapes with many items per compute unit take the one-stream kernel
+    (the 8192-token shard shape with all 28 heads among them): sampled rows of
+    every head against the oracle."""
+    require_gpu()
+    assert _one_stream(b, h, s), "shape no longer selects the one-stream kernel on this GPU"
+    q, k, v = _inputs(seed, b, h, s, d)
+    rows = sample_rows(s, 16, seed, must=(0, 63, 64, 127, 128, s - 1))
+    _check(f"one-stream {b}x{h}x{s}x{d}", q, k, v, 0, max(112, h), float(np.float32(1.0 / np.sqrt(d))), rows)
+
+
 # seq not a multiple of the 128-query or 64-key blocks; head_offset inside a
 # larger model; every head dimension.  (1,4,200,64) and (2,2,392,128) have an
 # even number of query blocks and (b, h) pairs a multiple of 4, so they take
