@@ -200,6 +200,101 @@ __device__ __forceinline__ void attn_block(AttnState<D>& st, const attn_lds_uint
   }
 }
 
+// An item: 128 consecutive queries (query block qb) of one (b, h).  Items are
+// numbered heaviest first (the causal work grows with the query block).  With
+// xcd_split, item j belongs to XCD j % 8: every (b, h) is cut into its even
+// and odd query blocks and XCD x takes half-heads [x*n, (x+1)*n), so an XCD's
+// L2 holds the K and V of at most n/2 + 1 heads.  Otherwise items walk query
+// blocks from the last to the first, every (b, h) at each step.
+struct AttnItem {
+  int qb;
+  int64_t bh;
+};
+__device__ __forceinline__ AttnItem attn_item(int j, int qblocks, int bh_count, bool xcd_split) {
+  AttnItem it;
+  if (xcd_split) {
+    const int x = j % 8, jj = j / 8;
+    const int n = bh_count / 4;  // half-heads per XCD
+    const int rank = jj / n, hh = n * x + jj % n, par = hh & 1;
+    it.bh = hh >> 1;
+    it.qb = qblocks - 1 - ((qblocks - 1 - par) & 1) - 2 * rank;
+  } else {
+    it.qb = qblocks - 1 - j / bh_count;
+    it.bh = j % bh_count;
+  }
+  return it;
+}
+
+// ALiBi offset fragments: k-slots 0..2 of the lower lane half carry the key
+// offset in the block (an integer < 64, exact in bf16) in kx, against
+// slope/scale split into three bf16 parts in qx; every other slot is zero.
+__device__ __forceinline__ void attn_key_offsets(bf16x8_t (&kx)[2], int half, int col) {
+  const __bf16 z = (__bf16)0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bool on = half == 0 && j < 3;
+    kx[0][j] = on ? (__bf16)(float)col : z;
+    kx[1][j] = on ? (__bf16)(float)(col + 32) : z;
+  }
+}
+__device__ __forceinline__ bf16x8_t attn_slope_parts(float slope2, float scale2, int half) {
+  const float cs = slope2 / scale2;  // slope/scale
+  const __bf16 c1 = (__bf16)cs;
+  const float r1 = cs - (float)c1;
+  const __bf16 c2 = (__bf16)r1;
+  const __bf16 c3 = (__bf16)(r1 - (float)c2);
+  const __bf16 z = (__bf16)0.0f;
+  bf16x8_t qx;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bool on = half == 0 && j < 3;
+    qx[j] = on ? (j == 0 ? c1 : (j == 1 ? c2 : c3)) : z;
+  }
+  return qx;
+}
+
+// Q^T operand fragments of a query row: lane supplies q[row][16*kk + 8*half .. +8]
+// (zeros past the sequence).
+template <int D>
+__device__ __forceinline__ void attn_load_q(bf16x8_t (&qf)[D / 16], const uint4* __restrict__ q, int64_t row, bool ok,
+                                            int half) {
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const uint4 u = ok ? q[row * (D / 8) + 2 * kk + half] : make_uint4(0u, 0u, 0u, 0u);
+    qf[kk] = as_bf16x8(u);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void attn_state_init(AttnState<D>& st) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.oacc[dt][i] = 0.f;
+  st.m = -INFINITY;
+  st.l = 0.f;
+}
+
+// Normalise and store a finished row: the two lane halves hold the sums over
+// complementary keys; lane half h holds d = 32*dt + 8*g + 4*h + 0..3.
+template <int D>
+__device__ __forceinline__ void attn_store_row(const AttnState<D>& st, uint2* __restrict__ o, float* __restrict__ lse,
+                                               int64_t row, bool ok, int half) {
+  const float l_tot = st.l + __shfl_xor(st.l, 32, kWave);
+  const float inv = 1.0f / l_tot;
+  if (!ok) return;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t lo = pack2(st.oacc[dt][4 * g] * inv, st.oacc[dt][4 * g + 1] * inv);
+      const uint32_t hi = pack2(st.oacc[dt][4 * g + 2] * inv, st.oacc[dt][4 * g + 3] * inv);
+      o[row * (D / 4) + (32 * dt + 8 * g + 4 * half) / 4] = make_uint2(lo, hi);
+    }
+  }
+  if (half == 0) lse[row] = (st.m + __log2f(l_tot)) * 0.69314718055994530942f;
+}
+
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_fwd_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
@@ -214,137 +309,73 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   __shared__ __attribute__((aligned(16))) uint4 tiles[2][2][2][CH];
   static_assert(sizeof(tiles) >= 4 * (DT * 16 + 2) * kWave * sizeof(float), "merge area");
 
+  // Two streams of four waves take the same 128 queries (wave w and w+4 the
+  // same 32) and alternate over the key blocks, so an item's serial chain is
+  // half its key blocks; their partial softmax states merge at the end.
   const int t = threadIdx.x;
   const int w = t / kWave, lane = t & (kWave - 1), half = lane >> 5, col = lane & 31;
   const int stream = w >> 2, wq = w & 3;
   attn_lds_uint4* lt = (attn_lds_uint4*)&tiles[0][0][0][0];
   auto tile = [&](int stage, int which) { return lt + ((stage * 2 + stream) * 2 + which) * CH; };
-
-  // ALiBi key-offset fragments (the same for every item): k-slots 0..2 of
-  // the lower lane half carry the key offset in the block.
   bf16x8_t kx[2];
-  {
-    const __bf16 z = (__bf16)0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool on = half == 0 && j < 3;
-      kx[0][j] = on ? (__bf16)(float)col : z;
-      kx[1][j] = on ? (__bf16)(float)(col + 32) : z;
-    }
-  }
+  attn_key_offsets(kx, half, col);
 
   // Persistent workgroups: the grid is a multiple of 8 and workgroup g runs
-  // on XCD g % 8.  Items (one 128-query block of one (b, h)) are numbered so
-  // that item j belongs to XCD j % 8 and, within an XCD, heaviest first; the
-  // U workgroups of an XCD take its items in a snake (round r: local item
-  // r*U + u for even r, r*U + U-1-u for odd r), which pairs heavy with light
-  // items.
+  // on XCD g % 8.  The U workgroups of an XCD take its items (j % 8 == x) in
+  // a snake (round r: local item r*U + u for even r, r*U + U-1-u for odd r),
+  // which pairs heavy items with light ones.
   const int U = (int)(gridDim.x / 8u), x8 = (int)(blockIdx.x % 8u), u = (int)(blockIdx.x / 8u);
   const int n_items = qblocks * bh_count;
-  // Item of round r of this workgroup: its (b, h) and query block, or none.
-  struct Item {
-    bool ok;
-    int qb;
-    int64_t bh;
-  };
-  auto item_of = [&](int r) {
-    Item it;
-    const int i_loc = r * U + ((r & 1) ? U - 1 - u : u);
-    const int j = i_loc * 8 + x8;
-    it.ok = j < n_items;
-    // Causal work grows with the query block.  With xcd_split every (b, h)
-    // is cut into its even and odd query blocks and XCD x takes half-heads
-    // [x*n, (x+1)*n), heaviest query block first, so an XCD's L2 holds the K
-    // and V of at most n/2 + 1 heads.  Otherwise items walk query blocks from
-    // the last to the first, every (b, h) at each step.
-    if (xcd_split) {
-      const int jj = j / 8;
-      const int n = bh_count / 4;  // half-heads per XCD
-      const int rank = jj / n, hh = n * x8 + jj % n, par = hh & 1;
-      it.bh = hh >> 1;
-      it.qb = qblocks - 1 - ((qblocks - 1 - par) & 1) - 2 * rank;
-    } else {
-      it.qb = qblocks - 1 - j / bh_count;
-      it.bh = j % bh_count;
-    }
-    return it;
-  };
-  // Q^T operand fragments of an item: lane supplies q[qi][16*kk + 8*half .. +8].
-  bf16x8_t qf[KS];
-  auto load_q = [&](const Item& it) {
-    const int qi_ = it.qb * kAttnBlockM + wq * 32 + col;
-    const bool ok = qi_ < seq;
-    const int64_t row = it.bh * (int64_t)seq + qi_;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const uint4 uq = ok ? q[row * (D / 8) + 2 * kk + half] : make_uint4(0u, 0u, 0u, 0u);
-      qf[kk] = as_bf16x8(uq);
-    }
-  };
+  auto item_index = [&](int r) { return (r * U + ((r & 1) ? U - 1 - u : u)) * 8 + x8; };
+  auto nkb_of = [&](int qb_) { return (min(seq, (qb_ + 1) * kAttnBlockM) - 1) / kAttnBlockN + 1; };
   // The first key block of an item for this stream (none if the item has
   // fewer blocks than streams), into stage 0.
-  auto request_first = [&](const Item& it) {
-    const int nkb_ = (min(seq, (it.qb + 1) * kAttnBlockM) - 1) / kAttnBlockN + 1;
-    const int kb_ = nkb_ - 1 - stream;
+  auto request_first = [&](const AttnItem& it) {
+    const int kb_ = nkb_of(it.qb) - 1 - stream;
     if (kb_ >= 0) {
       const int64_t base_ = it.bh * (int64_t)seq;
       attn_request<D, false>(k, tile(0, 0), base_, kb_ * kAttnBlockN, seq, wq, lane);
       attn_request<D, true>(v, tile(0, 1), base_, kb_ * kAttnBlockN, seq, wq, lane);
     }
   };
+  auto q_row = [&](const AttnItem& it) { return it.qb * kAttnBlockM + wq * 32 + col; };
 
-  Item cur = item_of(0);
-  if (!cur.ok) return;  // uniform over the workgroup
-  load_q(cur);
+  int j = item_index(0);
+  if (j >= n_items) return;  // uniform over the workgroup
+  AttnItem cur = attn_item(j, qblocks, bh_count, xcd_split);
+  bf16x8_t qf[KS];
+  attn_load_q<D>(qf, q, cur.bh * (int64_t)seq + q_row(cur), q_row(cur) < seq, half);
   request_first(cur);
   for (int r = 0;; ++r) {
     const int qb = cur.qb;
-    const int64_t bh = cur.bh;
-    const int h = (int)(bh % heads);
-    const float slope2 = slopes.s[h];
-    const int64_t base = bh * (int64_t)seq;  // row index of (b, h, 0)
+    const int64_t base = cur.bh * (int64_t)seq;  // row index of (b, h, 0)
+    const float slope2 = slopes.s[(int)(cur.bh % heads)];
     const int q0 = qb * kAttnBlockM + wq * 32;  // this wave's first query
     const int qi = q0 + col;                    // this lane's query
-    const bool qvalid = qi < seq;
     const bool wave_live = q0 < seq;
-    // slope/scale split into three bf16 parts against the key offsets of kx
-    bf16x8_t qx;
-    {
-      const float cs = slope2 / scale2;
-      const __bf16 c1 = (__bf16)cs;
-      const float r1 = cs - (float)c1;
-      const __bf16 c2 = (__bf16)r1;
-      const __bf16 c3 = (__bf16)(r1 - (float)c2);
-      const __bf16 z = (__bf16)0.0f;
-#pragma unroll
-      for (int jx = 0; jx < 8; ++jx) {
-        const bool on = half == 0 && jx < 3;
-        qx[jx] = on ? (jx == 0 ? c1 : (jx == 1 ? c2 : c3)) : z;
-      }
-    }
-
+    const bf16x8_t qx = attn_slope_parts(slope2, scale2, half);
     AttnState<D> st;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st.oacc[dt][i] = 0.f;
-    st.m = -INFINITY;
-    st.l = 0.f;
+    attn_state_init(st);
 
     // Key blocks run from the diagonal back to key 0 (stream s takes blocks
-    // nkb-1-s, nkb-3-s, ...); the first ones were requested already.
-    const int wg_last_q = min(seq, (qb + 1) * kAttnBlockM) - 1;
-    const int nkb = wg_last_q / kAttnBlockN + 1;
+    // nkb-1-s, nkb-3-s, ...): the block holding a row's own key comes first,
+    // and with the ALiBi bias falling off with distance the running max then
+    // rarely moves.  The first ones were requested already.
+    const int nkb = nkb_of(qb);
     const int iters = (nkb + 1) / 2;
     int kb = nkb - 1 - stream;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     for (int it = 0, buf = 0; it < iters; ++it, buf ^= 1, kb -= 2) {
       const int k0 = kb * kAttnBlockN;
+      // the next block's transfers run during this block's products (the
+      // barrier that ended the previous iteration freed their buffer)
       if (kb >= 2) {
         attn_request<D, false>(k, tile(buf ^ 1, 0), base, k0 - 2 * kAttnBlockN, seq, wq, lane);
         attn_request<D, true>(v, tile(buf ^ 1, 1), base, k0 - 2 * kAttnBlockN, seq, wq, lane);
       }
+      // Every processed block has k0 <= q0 (both are multiples of 32), so each
+      // row has its key k0 unmasked and the first block sets a finite max.
       if (kb >= 0 && wave_live && k0 <= q0 + 31) {
         if (k0 + kAttnBlockN - 1 > q0)
           attn_block<D, true>(st, tile(buf, 0), tile(buf, 1), qf, kx, qx, scale2, slope2, k0, qi, half, col, lane);
@@ -356,10 +387,14 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     }
 
     // The next item's Q arrives during the merge (this item's Q is done).
-    const Item nxt = item_of(r + 1);
-    if (nxt.ok) load_q(nxt);
+    const int jn = item_index(r + 1);
+    const bool has_next = jn < n_items;
+    const AttnItem nxt = attn_item(has_next ? jn : j, qblocks, bh_count, xcd_split);
+    if (has_next) attn_load_q<D>(qf, q, nxt.bh * (int64_t)seq + q_row(nxt), q_row(nxt) < seq, half);
 
     // Merge stream 1 into stream 0 through LDS ([wave][value][lane] floats).
+    // Block 0 is processed by one of the streams for every live row, so at
+    // least one of the two maxima is finite.
     float* mg = reinterpret_cast<float*>(&tiles[0][0][0][0]) + wq * (DT * 16 + 2) * kWave + lane;
     if (stream == 1) {
 #pragma unroll
@@ -384,30 +419,12 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     // The merge area is the next item's tile memory: every read of it ends
     // here, and the next item's first key blocks are requested right after.
     __syncthreads();
-    if (nxt.ok) request_first(nxt);
-    if (stream == 0) {
-      // Normalise: the two lane halves hold the sums over complementary keys.
-      const float l_tot = st.l + __shfl_xor(st.l, 32, kWave);
-      const float inv = 1.0f / l_tot;
-      if (qvalid) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            // d = 32*dt + 8*g + 4*half + 0..3
-            const uint32_t lo = pack2(st.oacc[dt][4 * g] * inv, st.oacc[dt][4 * g + 1] * inv);
-            const uint32_t hi = pack2(st.oacc[dt][4 * g + 2] * inv, st.oacc[dt][4 * g + 3] * inv);
-            o[(base + qi) * (D / 4) + (32 * dt + 8 * g + 4 * half) / 4] = make_uint2(lo, hi);
-          }
-        }
-        if (half == 0) lse[base + qi] = (st.m + __log2f(l_tot)) * 0.69314718055994530942f;
-      }
-    }
-    if (!nxt.ok) break;  // uniform over the workgroup
+    if (has_next) request_first(nxt);
+    if (stream == 0) attn_store_row<D>(st, o, lse, base + qi, qi < seq, half);
+    if (!has_next) break;  // uniform over the workgroup
+    j = jn;
     cur = nxt;
   }
-  // The last transfers issued (none after the final item) have landed: the
-  // loop's waits covered every request.
 }
 
 // The same forward with one key stream per workgroup: four waves take the
@@ -416,72 +433,34 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
 // Two independent workgroups per unit hide each other's start-up and
 // output stores, which wins when every unit gets many items (long
 // sequences); the two-stream kernel halves the longest item's chain, which
-// wins when the longest item is a large share of a unit's work.
+// wins when the longest item is a large share of a unit's work.  Workgroup i
+// takes item i (heaviest first; on XCD i % 8 with xcd_split).
 template <int D>
 __global__ __launch_bounds__(kAttnGroupThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_fwd_stream_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
     uint2* __restrict__ o, float* __restrict__ lse, int seq, int heads, int qblocks, int bh_count,
     bool xcd_split, float scale2, AttnSlopes slopes) {
   constexpr int KS = D / 16;
-  constexpr int DT = D / 32;
-  constexpr int VPR = D / 8;
   constexpr int CH = AttnTile<D>::CHUNKS;
   __shared__ __attribute__((aligned(16))) uint4 tiles[2][2][CH];  // [stage][K, V]
 
   const int t = threadIdx.x;
   const int w = t / kWave, lane = t & (kWave - 1), half = lane >> 5, col = lane & 31;
-  // Workgroup i runs on XCD i % 8; the items are mapped as in the two-stream
-  // kernel (each XCD takes a contiguous range of half-heads), heaviest first.
-  int qb;
-  int64_t bh;
-  if (xcd_split) {
-    const int x = (int)(blockIdx.x % 8u), j = (int)(blockIdx.x / 8u);
-    const int n = bh_count / 4;  // half-heads per XCD
-    const int rank = j / n, hh = n * x + j % n, par = hh & 1;
-    bh = hh >> 1;
-    qb = qblocks - 1 - ((qblocks - 1 - par) & 1) - 2 * rank;
-  } else {
-    qb = qblocks - 1 - (int)(blockIdx.x / (unsigned)bh_count);
-    bh = blockIdx.x % (unsigned)bh_count;
-  }
-  const int h = (int)(bh % heads);
-  const float slope2 = slopes.s[h];
-  const int64_t base = bh * (int64_t)seq;
+  const AttnItem it = attn_item((int)blockIdx.x, qblocks, bh_count, xcd_split);
+  const int qb = it.qb;
+  const int64_t base = it.bh * (int64_t)seq;
+  const float slope2 = slopes.s[(int)(it.bh % heads)];
   const int q0 = qb * kAttnBlockM + w * 32;
   const int qi = q0 + col;
-  const bool qvalid = qi < seq;
   const bool wave_live = q0 < seq;
 
   bf16x8_t qf[KS];
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    const uint4 u = qvalid ? q[(base + qi) * VPR + 2 * kk + half] : make_uint4(0u, 0u, 0u, 0u);
-    qf[kk] = as_bf16x8(u);
-  }
-  bf16x8_t kx[2], qx;
-  {
-    const float cs = slope2 / scale2;
-    const __bf16 c1 = (__bf16)cs;
-    const float r1 = cs - (float)c1;
-    const __bf16 c2 = (__bf16)r1;
-    const __bf16 c3 = (__bf16)(r1 - (float)c2);
-    const __bf16 z = (__bf16)0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool on = half == 0 && j < 3;
-      qx[j] = on ? (j == 0 ? c1 : (j == 1 ? c2 : c3)) : z;
-      kx[0][j] = on ? (__bf16)(float)col : z;
-      kx[1][j] = on ? (__bf16)(float)(col + 32) : z;
-    }
-  }
-
+  attn_load_q<D>(qf, q, base + qi, qi < seq, half);
+  bf16x8_t kx[2];
+  attn_key_offsets(kx, half, col);
+  const bf16x8_t qx = attn_slope_parts(slope2, scale2, half);
   AttnState<D> st;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) st.oacc[dt][i] = 0.f;
-  st.m = -INFINITY;
-  st.l = 0.f;
+  attn_state_init(st);
 
   const int wg_last_q = min(seq, (qb + 1) * kAttnBlockM) - 1;
   const int nkb = wg_last_q / kAttnBlockN + 1;
@@ -507,20 +486,7 @@ __global__ __launch_bounds__(kAttnGroupThreads) __attribute__((amdgpu_waves_per_
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
-  const float l_tot = st.l + __shfl_xor(st.l, 32, kWave);
-  const float inv = 1.0f / l_tot;
-  if (qvalid) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t lo = pack2(st.oacc[dt][4 * g] * inv, st.oacc[dt][4 * g + 1] * inv);
-        const uint32_t hi = pack2(st.oacc[dt][4 * g + 2] * inv, st.oacc[dt][4 * g + 3] * inv);
-        o[(base + qi) * (D / 4) + (32 * dt + 8 * g + 4 * half) / 4] = make_uint2(lo, hi);
-      }
-    }
-    if (half == 0) lse[base + qi] = (st.m + __log2f(l_tot)) * 0.69314718055994530942f;
-  }
+  attn_store_row<D>(st, o, lse, base + qi, qi < seq, half);
 }
 
 bloom_status check_attention(int64_t batch, int32_t heads, int64_t seq, int32_t head_dim) {
