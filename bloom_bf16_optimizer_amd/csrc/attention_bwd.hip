@@ -10,15 +10,17 @@
 //   dq_i  = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
 //   dv_j  = sum_i p_ij dO_i.
 //
-// Two kernels, each owning its outputs (no atomics, results independent of
+// Three kernels, each owning its outputs (no atomics, results independent of
 // scheduling):
-//  * dq: a workgroup of four waves takes 128 consecutive queries of one (b, h),
-//    a wave 32, and streams the key blocks (64 keys, K and V staged in LDS)
-//    up to its diagonal, twice.  Both passes form S^T = K Q^T and dP^T = V dO^T
-//    so that lane l owns query l%32 (its lse and D_i are one number each).
-//    The first pass sums D_i = sum_j p_ij dp_ij in FP32; the second forms dS
-//    and dQ^T += K^T dS^T with K^T read from the same LDS tile by the
-//    transposing ds_read_b64_tr_b16.  It also writes D_i for the second kernel.
+//  * D and dq: two kernels with one body.  A workgroup of four waves takes
+//    128 consecutive queries of one (b, h), a wave 32, and streams the key
+//    blocks (64 keys, K and V staged in LDS) up to its diagonal once.  Both
+//    form S^T = K Q^T and dP^T = V dO^T so that lane l owns query l%32 (its
+//    lse and D_i are one number each).  The D kernel sums
+//    D_i = sum_j p_ij dp_ij in FP32 and writes it to the workspace; the dq
+//    kernel reads it back, forms dS and dQ^T += K^T dS^T with K^T read from
+//    the same LDS tile by the transposing ds_read_b64_tr_b16.  Apart, each
+//    fits the 256 registers that let two waves share a SIMD.
 //    (The usual shortcut D_i = dO_i . o_i from the stored bf16 o carries that
 //    rounding, 2^-9 of sum_d |dO_id o_id|, into every ds_ij of the row at
 //    weight p_ij; with ALiBi's steep slopes p is often near 1 on the diagonal
@@ -115,10 +117,12 @@ __device__ __forceinline__ Bf16Pair split_bf16(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// dq kernel: one key block for one wave.  s, dp: rows = keys
-// k0 + 32*kt + 8*(i/4) + 4*half + i%4, column = this lane's query qi.
-// SUM: the first pass, which only adds p * dp into dsum; otherwise the
-// second, which forms dS with the row's D = delta and accumulates dQ^T.
+// Query-side passes: one key block for one wave.  s, dp: rows = keys
+// k0 + 32*kt + 8*(i/4) + 4*half + i%4, column = this lane's query qi.  The
+// block is taken as two 32-key halves (kt = 0, 1) so that only one half's S,
+// dP and dS are live at a time.  SUM: the D pass, which only adds p * dp into
+// dsum; otherwise the dq pass, which forms dS with the row's D = delta and
+// accumulates dQ^T over the half's two 16-key steps right after forming it.
 template <int D, bool DIAG, bool SUM>
 __device__ __forceinline__ void dq_block(f32x16_t (&acc)[D / 32], float& dsum, const attn_lds_uint4* __restrict__ kt_lds,
                                          const attn_lds_uint4* __restrict__ vt_lds, const bf16x8_t (&qf)[D / 16],
@@ -127,59 +131,72 @@ __device__ __forceinline__ void dq_block(f32x16_t (&acc)[D / 32], float& dsum, c
   using T = BwdTile<D>;
   constexpr int KS = D / 16, DT = D / 32;
   const f32x16_t zero = {};
-  f32x16_t s[2] = {zero, zero}, dp[2] = {zero, zero};
   const int sw = T::swz(col);  // also the swizzle of row col + 32
   const attn_lds_u32x4* k0r = reinterpret_cast<const attn_lds_u32x4*>(kt_lds) + col * T::CPR;
   const attn_lds_u32x4* v0r = reinterpret_cast<const attn_lds_u32x4*>(vt_lds) + col * T::CPR;
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    const int c = (2 * kk + half) ^ sw;
-    s[0] = mfma32(__builtin_bit_cast(bf16x8_t, k0r[c]), qf[kk], s[0]);
-    s[1] = mfma32(__builtin_bit_cast(bf16x8_t, k0r[32 * T::CPR + c]), qf[kk], s[1]);
-    dp[0] = mfma32(__builtin_bit_cast(bf16x8_t, v0r[c]), df[kk], dp[0]);
-    dp[1] = mfma32(__builtin_bit_cast(bf16x8_t, v0r[32 * T::CPR + c]), df[kk], dp[1]);
-  }
   // base-2 logit minus lse: s*scale2 + slope2*(key - qi) - lse2
   const float cb = fmaf(slope2, (float)(k0 + 4 * half - qi), -lse2);
-  bf16x8_t dsh[4], dsl[4];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int off = 32 * kt + 8 * (i / 4) + (i % 4);  // key - k0 - 4*half
-      float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], scale2, fmaf(slope2, (float)off, cb)));
-      if (DIAG && k0 + 4 * half + off > qi) p = 0.f;
-      if (SUM) {
-        dsum = fmaf(p, dp[kt][i], dsum);
-      } else {
-        const Bf16Pair d2 = split_bf16(p * (dp[kt][i] - delta));
-        dsh[2 * kt + i / 8][i % 8] = d2.hi;
-        dsl[2 * kt + i / 8][i % 8] = d2.lo;
-      }
-    }
-  if (SUM) return;
-  // dQ^T += K^T dS^T over the 4 key steps of the block
+  // transposing reads of K for dQ^T += K^T dS^T
   const int tj = (lane & 15) >> 2, tc = lane & 3, tg = (lane >> 4) & 1;
   const int trow = 4 * half + tj;
   const int sw0 = T::swz(trow), sw8 = T::swz(trow + 8);  // the same for every step (rows + 16)
   const char __attribute__((address_space(3)))* kbytes =
       reinterpret_cast<const char __attribute__((address_space(3)))*>(kt_lds);
 #pragma unroll
-  for (int stp = 0; stp < 4; ++stp)
+  for (int kt = 0; kt < 2; ++kt) {
+    f32x16_t s = zero, dp = zero;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const bf16x8_t kT = bwd_read_tr<D>(kbytes, 16 * stp, dt, trow, tg, tc, sw0, sw8);
-      acc[dt] = mfma32(kT, dsh[stp], acc[dt]);
-      acc[dt] = mfma32(kT, dsl[stp], acc[dt]);
+    for (int kk = 0; kk < KS; ++kk) {
+      const int c = 32 * kt * T::CPR + ((2 * kk + half) ^ sw);
+      s = mfma32(__builtin_bit_cast(bf16x8_t, k0r[c]), qf[kk], s);
+      dp = mfma32(__builtin_bit_cast(bf16x8_t, v0r[c]), df[kk], dp);
     }
+    bf16x8_t dsh[2], dsl[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int off = 32 * kt + 8 * (i / 4) + (i % 4);  // key - k0 - 4*half
+      float p = __builtin_amdgcn_exp2f(fmaf(s[i], scale2, fmaf(slope2, (float)off, cb)));
+      if (DIAG && k0 + 4 * half + off > qi) p = 0.f;
+      if (SUM) {
+        dsum = fmaf(p, dp[i], dsum);
+      } else {
+        const Bf16Pair d2 = split_bf16(p * (dp[i] - delta));
+        dsh[i / 8][i % 8] = d2.hi;
+        dsl[i / 8][i % 8] = d2.lo;
+      }
+    }
+    if (!SUM) {
+#pragma unroll
+      for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x8_t kT = bwd_read_tr<D>(kbytes, 16 * (2 * kt + st2), dt, trow, tg, tc, sw0, sw8);
+          acc[dt] = mfma32(kT, dsh[st2], acc[dt]);
+          acc[dt] = mfma32(kT, dsl[st2], acc[dt]);
+        }
+    }
+  }
 }
 
-template <int D>
-__global__ __launch_bounds__(kBwdThreads) void attention_bwd_dq_kernel(
-    const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
-    const uint4* __restrict__ dout, const float* __restrict__ lse, uint2* __restrict__ dq,
-    float* __restrict__ delta_out, int seq, int heads, int qblocks, int bh_count,
-    float scale2, float scale, AttnSlopes slopes) {
+// The two query-side kernels share one body: a workgroup of four waves takes
+// items of 128 queries of one (b, h), a wave 32, and streams the key blocks
+// (64 keys, K and V staged in LDS) from its diagonal down to key 0 once.  SUM:
+// the D pass, which writes D_i = sum_j p_ij dp_ij to `delta`; otherwise the
+// dq pass, which reads it back and writes dq.
+//
+// Persistent workgroups, two per compute unit: a workgroup takes items
+// (numbered longest first: item j is query block qblocks-1-j/bh_count of
+// (b, h) = j % bh_count) in a snake over the grid (round r: item r*G + g for
+// even r, r*G + G-1-g for odd r), so heavy items pair with light ones.  While
+// an item's last key block is used, the next item's first block is already on
+// its way, and the next item's rows are loaded before this item's result is
+// stored.
+template <int D, bool SUM>
+__device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, const uint4* __restrict__ k,
+                                               const uint4* __restrict__ v, const uint4* __restrict__ dout,
+                                               const float* __restrict__ lse, float* __restrict__ delta_io,
+                                               uint2* __restrict__ dq, int seq, int heads, int qblocks, int bh_count,
+                                               float scale2, float scale, const AttnSlopes& slopes) {
   constexpr int KS = D / 16, DT = D / 32, VPR = D / 8;
   constexpr int CH = BwdTile<D>::CHUNKS;
   __shared__ __attribute__((aligned(16))) uint4 tiles[2][2][CH];  // [stage][K, V]
@@ -189,14 +206,6 @@ __global__ __launch_bounds__(kBwdThreads) void attention_bwd_dq_kernel(
   attn_lds_uint4* lt = (attn_lds_uint4*)&tiles[0][0][0];
   auto tile = [&](int stage, int which) { return lt + (stage * 2 + which) * CH; };
 
-  // Persistent workgroups: a workgroup takes items (128 queries of one (b, h),
-  // numbered longest first: item j is query block qblocks-1-j/bh_count of
-  // (b, h) = j % bh_count) in a snake over the grid (round r: item r*G + g
-  // for even r, r*G + G-1-g for odd r), so heavy items pair with light ones.
-  // While an item's last key block is used, the next stage's first block is
-  // already on its way: the second pass's during the first pass, the next
-  // item's during the second, with the next item's q and dO rows loaded
-  // before this item's dq is stored.
   const int G = (int)gridDim.x, g = (int)blockIdx.x;
   const int n_items = qblocks * bh_count;
   auto item_j = [&](int r) { return r * G + ((r & 1) ? G - 1 - g : g); };
@@ -206,21 +215,27 @@ __global__ __launch_bounds__(kBwdThreads) void attention_bwd_dq_kernel(
   if (j >= n_items) return;  // uniform over the workgroup
   // B operands: this lane's query row of q and dO (d = 16*kk + 8*half .. +8)
   bf16x8_t qf[KS], df[KS];
-  float lse2;
+  float lse2, delta = 0.f;
   auto load_rows = [&](int jn) {
     const int qb_ = qblocks - 1 - jn / bh_count;
     const int64_t bh_ = jn % bh_count;
     const int qi_ = qb_ * kBwdBlock + w * 32 + col;
     const bool ok = qi_ < seq;
-    const int64_t row = bh_ * (int64_t)seq + qi_;
+    // rows past seq read row seq-1 and are then zeroed (no branches)
+    const int64_t row = bh_ * (int64_t)seq + min(qi_, seq - 1);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
       const int64_t idx = row * VPR + 2 * kk + half;
-      qf[kk] = as_bf16x8(ok ? q[idx] : z4);
-      df[kk] = as_bf16x8(ok ? dout[idx] : z4);
+      const uint4 a = q[idx], b = dout[idx];
+      qf[kk] = as_bf16x8(ok ? a : make_uint4(0u, 0u, 0u, 0u));
+      df[kk] = as_bf16x8(ok ? b : make_uint4(0u, 0u, 0u, 0u));
     }
-    lse2 = ok ? lse[row] * kLog2e : 0.f;
+    const float l = lse[row];
+    lse2 = ok ? l * kLog2e : 0.f;
+    if (!SUM) {
+      const float d = delta_io[row];
+      delta = ok ? d : 0.f;
+    }
   };
   auto request_block = [&](int jn, int kb_, int stage) {
     const int64_t base_ = (int64_t)(jn % bh_count) * seq;
@@ -244,56 +259,43 @@ __global__ __launch_bounds__(kBwdThreads) void attention_bwd_dq_kernel(
     const bool has_next = jn < n_items;
 
     f32x16_t acc[DT];
+    if (!SUM) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
-
-    const int nkb = nkb_of(qb);  // key blocks nkb-1 .. 0, streamed once per pass
-    float dsum = 0.f, delta = 0.f;
+        for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+    }
+    float dsum = 0.f;
+    const int nkb = nkb_of(qb);  // key blocks nkb-1 .. 0
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    for (int pass = 0; pass < 2; ++pass) {
-      for (int kb = nkb - 1; kb >= 0; --kb, buf ^= 1) {
-        const int k0 = kb * kBwdRows;
-        // the next block arrives while this one is used (the barrier that
-        // ended the previous iteration freed its buffer)
-        if (kb >= 1)
-          request_block(j, kb - 1, buf ^ 1);
-        else if (pass == 0)
-          request_block(j, nkb - 1, buf ^ 1);
-        else if (has_next)
-          request_block(jn, nkb_of(qblocks - 1 - jn / bh_count) - 1, buf ^ 1);
-        if (wave_live && k0 <= q0 + 31) {
-          const bool diag = k0 + kBwdRows - 1 > q0;
-          if (pass == 0) {
-            if (diag)
-              dq_block<D, true, true>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta, k0,
-                                      qi, half, col, lane);
-            else
-              dq_block<D, false, true>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta,
-                                       k0, qi, half, col, lane);
-          } else {
-            if (diag)
-              dq_block<D, true, false>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta,
-                                       k0, qi, half, col, lane);
-            else
-              dq_block<D, false, false>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta,
-                                        k0, qi, half, col, lane);
-          }
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+    for (int kb = nkb - 1; kb >= 0; --kb, buf ^= 1) {
+      const int k0 = kb * kBwdRows;
+      // the next block arrives while this one is used (the barrier that
+      // ended the previous iteration freed its buffer)
+      if (kb >= 1)
+        request_block(j, kb - 1, buf ^ 1);
+      else if (has_next)
+        request_block(jn, nkb_of(qblocks - 1 - jn / bh_count) - 1, buf ^ 1);
+      if (wave_live && k0 <= q0 + 31) {
+        if (k0 + kBwdRows - 1 > q0)
+          dq_block<D, true, SUM>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta, k0, qi,
+                                 half, col, lane);
+        else
+          dq_block<D, false, SUM>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta, k0,
+                                  qi, half, col, lane);
       }
-      if (pass == 0) {
-        // the two lane halves summed complementary keys of the same query
-        delta = dsum + __shfl_xor(dsum, 32, kWave);
-        if (qvalid && half == 0) delta_out[base + qi] = delta;
-      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
     }
-    // this item's q, dO and lse are no longer needed: the next item's load now
+    if (SUM) {
+      // the two lane halves summed complementary keys of the same query
+      const float dl = dsum + __shfl_xor(dsum, 32, kWave);
+      if (qvalid && half == 0) delta_io[base + qi] = dl;
+    }
+    // this item's q, dO, lse and D are no longer needed: the next item's load now
     if (has_next) load_rows(jn);
-    if (qvalid) {
+    if (!SUM && qvalid) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -307,6 +309,25 @@ __global__ __launch_bounds__(kBwdThreads) void attention_bwd_dq_kernel(
     if (!has_next) break;  // uniform over the workgroup
     j = jn;
   }
+}
+
+// D pass: writes D_i for every query (FP32, [b*h*seq]).
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_bwd_delta_kernel(
+    const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
+    const uint4* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ delta, int seq, int heads,
+    int qblocks, int bh_count, float scale2, AttnSlopes slopes) {
+  bwd_query_pass<D, true>(q, k, v, dout, lse, delta, nullptr, seq, heads, qblocks, bh_count, scale2, 1.f, slopes);
+}
+
+// dq pass: dq_i = scale * sum_j ds_ij k_j with D_i from the D pass.
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_bwd_dq_kernel(
+    const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
+    const uint4* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ delta,
+    uint2* __restrict__ dq, int seq, int heads, int qblocks, int bh_count, float scale2, float scale,
+    AttnSlopes slopes) {
+  bwd_query_pass<D, false>(q, k, v, dout, lse, delta, dq, seq, heads, qblocks, bh_count, scale2, scale, slopes);
 }
 
 // ---------------------------------------------------------------------------
@@ -488,16 +509,18 @@ void launch_bwd(const bloom_bf16* q, const bloom_bf16* k, const bloom_bf16* v, c
   const int bh_count = (int)(batch * heads);
   const int blocks = (int)((seq + kBwdBlock - 1) / kBwdBlock);
   const dim3 grid((unsigned)(bh_count * blocks));
-  // the dq kernel is persistent: one workgroup per compute unit, at most one per item
+  // the D and dq kernels are persistent: two workgroups per compute unit, at most one per item
   const int64_t n_items = (int64_t)bh_count * blocks;
-  const int cus = device_cu_count();
-  const dim3 grid_dq((unsigned)(n_items < cus ? n_items : (cus > 0 ? cus : 1)));
+  const int64_t slots = 2 * (int64_t)(device_cu_count() > 0 ? device_cu_count() : 1);
+  const dim3 grid_q((unsigned)(n_items < slots ? n_items : slots));
   const uint4* qv = reinterpret_cast<const uint4*>(q);
   const uint4* kv = reinterpret_cast<const uint4*>(k);
   const uint4* vv = reinterpret_cast<const uint4*>(v);
   const uint4* dov = reinterpret_cast<const uint4*>(dout);
-  hipLaunchKernelGGL((attention_bwd_dq_kernel<D>), grid_dq, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov, lse,
-                     reinterpret_cast<uint2*>(dq), delta, (int)seq, (int)heads, blocks, bh_count, scale2, scale,
+  hipLaunchKernelGGL((attention_bwd_delta_kernel<D>), grid_q, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov, lse,
+                     delta, (int)seq, (int)heads, blocks, bh_count, scale2, table);
+  hipLaunchKernelGGL((attention_bwd_dq_kernel<D>), grid_q, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov, lse,
+                     delta, reinterpret_cast<uint2*>(dq), (int)seq, (int)heads, blocks, bh_count, scale2, scale,
                      table);
   hipLaunchKernelGGL((attention_bwd_dkdv_kernel<D>), grid, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov, lse,
                      delta, reinterpret_cast<uint2*>(dk), reinterpret_cast<uint2*>(dv), (int)seq, (int)heads,
