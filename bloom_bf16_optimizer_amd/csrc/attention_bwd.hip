@@ -13,8 +13,10 @@
 // Three kernels, each owning its outputs (no atomics, results independent of
 // scheduling):
 //  * D and dq: two kernels with one body.  A workgroup of four waves takes
-//    128 consecutive queries of one (b, h), a wave 32, and streams the key
-//    blocks (64 keys, K and V staged in LDS) up to its diagonal once.  Both
+//    128 consecutive queries of one (b, h), a wave 32 (or, in launches with
+//    few query blocks, 64 queries, a wave 32 of them against half the keys),
+//    and streams the key blocks (64 keys, K and V staged in LDS) up to its
+//    diagonal once.  Both
 //    form S^T = K Q^T and dP^T = V dO^T so that lane l owns query l%32 (its
 //    lse and D_i are one number each).  The D kernel sums
 //    D_i = sum_j p_ij dp_ij in FP32 and writes it to the workspace; the dq
@@ -119,15 +121,16 @@ __device__ __forceinline__ Bf16Pair split_bf16(float x) {
 // ---------------------------------------------------------------------------
 // Query-side passes: one key block for one wave.  s, dp: rows = keys
 // k0 + 32*kt + 8*(i/4) + 4*half + i%4, column = this lane's query qi.  The
-// block is taken as two 32-key halves (kt = 0, 1) so that only one half's S,
-// dP and dS are live at a time.  SUM: the D pass, which only adds p * dp into
-// dsum; otherwise the dq pass, which forms dS with the row's D = delta and
-// accumulates dQ^T over the half's two 16-key steps right after forming it.
-template <int D, bool DIAG, bool SUM>
+// wave takes the block's 32-key halves kt0 .. kt0+NKT-1 (both, or one), one
+// at a time, so that only one half's S, dP and dS are live.  SUM: the D pass,
+// which only adds p * dp into dsum; otherwise the dq pass, which forms dS with
+// the row's D = delta and accumulates dQ^T over the half's two 16-key steps
+// right after forming it.
+template <int D, bool DIAG, bool SUM, int NKT>
 __device__ __forceinline__ void dq_block(f32x16_t (&acc)[D / 32], float& dsum, const attn_lds_uint4* __restrict__ kt_lds,
                                          const attn_lds_uint4* __restrict__ vt_lds, const bf16x8_t (&qf)[D / 16],
                                          const bf16x8_t (&df)[D / 16], float scale2, float slope2, float lse2,
-                                         float delta, int k0, int qi, int half, int col, int lane) {
+                                         float delta, int k0, int kt0, int qi, int half, int col, int lane) {
   using T = BwdTile<D>;
   constexpr int KS = D / 16, DT = D / 32;
   const f32x16_t zero = {};
@@ -143,7 +146,8 @@ __device__ __forceinline__ void dq_block(f32x16_t (&acc)[D / 32], float& dsum, c
   const char __attribute__((address_space(3)))* kbytes =
       reinterpret_cast<const char __attribute__((address_space(3)))*>(kt_lds);
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int u = 0; u < NKT; ++u) {
+    const int kt = kt0 + u;
     f32x16_t s = zero, dp = zero;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -179,10 +183,14 @@ __device__ __forceinline__ void dq_block(f32x16_t (&acc)[D / 32], float& dsum, c
 }
 
 // The two query-side kernels share one body: a workgroup of four waves takes
-// items of 128 queries of one (b, h), a wave 32, and streams the key blocks
-// (64 keys, K and V staged in LDS) from its diagonal down to key 0 once.  SUM:
-// the D pass, which writes D_i = sum_j p_ij dp_ij to `delta`; otherwise the
-// dq pass, which reads it back and writes dq.
+// items of QI consecutive queries of one (b, h) and streams the key blocks
+// (64 keys, K and V staged in LDS) from its diagonal down to key 0 once.
+// QI = 128: wave w takes queries 32w .. +31 against all 64 keys of a block.
+// QI = 64: wave w takes queries 32*(w%2) .. +31 against the block's keys
+// 32*(w/2) .. +31; the two waves of a query tile add their halves through LDS
+// at the end of the item (twice the items, for launches with few of them).
+// SUM: the D pass, which writes D_i = sum_j p_ij dp_ij to `delta`; otherwise
+// the dq pass, which reads it back and writes dq.
 //
 // Persistent workgroups, two per compute unit: a workgroup takes items
 // (numbered longest first: item j is query block qblocks-1-j/bh_count of
@@ -191,25 +199,29 @@ __device__ __forceinline__ void dq_block(f32x16_t (&acc)[D / 32], float& dsum, c
 // an item's last key block is used, the next item's first block is already on
 // its way, and the next item's rows are loaded before this item's result is
 // stored.
-template <int D, bool SUM>
+template <int D, bool SUM, int QI>
 __device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, const uint4* __restrict__ k,
                                                const uint4* __restrict__ v, const uint4* __restrict__ dout,
                                                const float* __restrict__ lse, float* __restrict__ delta_io,
                                                uint2* __restrict__ dq, int seq, int heads, int qblocks, int bh_count,
                                                float scale2, float scale, const AttnSlopes& slopes) {
+  static_assert(QI == 64 || QI == 128, "items of 64 or 128 queries");
   constexpr int KS = D / 16, DT = D / 32, VPR = D / 8;
   constexpr int CH = BwdTile<D>::CHUNKS;
+  constexpr int NKT = QI / 64;  // 32-key halves of a block per wave
   __shared__ __attribute__((aligned(16))) uint4 tiles[2][2][CH];  // [stage][K, V]
 
   const int t = threadIdx.x;
   const int w = t / kWave, lane = t & (kWave - 1), half = lane >> 5, col = lane & 31;
+  const int qt = QI == 128 ? w : (w & 1);  // this wave's 32-query tile within the item
+  const int kh = QI == 128 ? 0 : (w >> 1);  // its first 32-key half of each block
   attn_lds_uint4* lt = (attn_lds_uint4*)&tiles[0][0][0];
   auto tile = [&](int stage, int which) { return lt + (stage * 2 + which) * CH; };
 
   const int G = (int)gridDim.x, g = (int)blockIdx.x;
   const int n_items = qblocks * bh_count;
   auto item_j = [&](int r) { return r * G + ((r & 1) ? G - 1 - g : g); };
-  auto nkb_of = [&](int qb_) { return (min(seq, (qb_ + 1) * kBwdBlock) - 1) / kBwdRows + 1; };
+  auto nkb_of = [&](int qb_) { return (min(seq, (qb_ + 1) * QI) - 1) / kBwdRows + 1; };
 
   int j = item_j(0);
   if (j >= n_items) return;  // uniform over the workgroup
@@ -219,7 +231,7 @@ __device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, cons
   auto load_rows = [&](int jn) {
     const int qb_ = qblocks - 1 - jn / bh_count;
     const int64_t bh_ = jn % bh_count;
-    const int qi_ = qb_ * kBwdBlock + w * 32 + col;
+    const int qi_ = qb_ * QI + qt * 32 + col;
     const bool ok = qi_ < seq;
     // rows past seq read row seq-1 and are then zeroed (no branches)
     const int64_t row = bh_ * (int64_t)seq + min(qi_, seq - 1);
@@ -251,7 +263,7 @@ __device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, cons
     const int h = (int)(bh % heads);
     const float slope2 = slopes.s[h];
     const int64_t base = bh * (int64_t)seq;
-    const int q0 = qb * kBwdBlock + w * 32;
+    const int q0 = qb * QI + qt * 32;  // this wave's first query
     const int qi = q0 + col;
     const bool qvalid = qi < seq;
     const bool wave_live = q0 < seq;
@@ -271,31 +283,58 @@ __device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, cons
     __syncthreads();
     for (int kb = nkb - 1; kb >= 0; --kb, buf ^= 1) {
       const int k0 = kb * kBwdRows;
+      const int kw0 = k0 + 32 * kh;  // this wave's first key of the block
       // the next block arrives while this one is used (the barrier that
       // ended the previous iteration freed its buffer)
       if (kb >= 1)
         request_block(j, kb - 1, buf ^ 1);
       else if (has_next)
         request_block(jn, nkb_of(qblocks - 1 - jn / bh_count) - 1, buf ^ 1);
-      if (wave_live && k0 <= q0 + 31) {
-        if (k0 + kBwdRows - 1 > q0)
-          dq_block<D, true, SUM>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta, k0, qi,
-                                 half, col, lane);
+      if (wave_live && kw0 <= q0 + 31) {
+        if (kw0 + 32 * NKT - 1 > q0)
+          dq_block<D, true, SUM, NKT>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta, k0,
+                                      kh, qi, half, col, lane);
         else
-          dq_block<D, false, SUM>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta, k0,
-                                  qi, half, col, lane);
+          dq_block<D, false, SUM, NKT>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta,
+                                       k0, kh, qi, half, col, lane);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
-    if (SUM) {
-      // the two lane halves summed complementary keys of the same query
-      const float dl = dsum + __shfl_xor(dsum, 32, kWave);
-      if (qvalid && half == 0) delta_io[base + qi] = dl;
+    // the two lane halves summed complementary keys of the same query
+    float dl = 0.f;
+    if (SUM) dl = dsum + __shfl_xor(dsum, 32, kWave);
+    if (QI == 64) {
+      // the key-half-1 waves hand their sums to the key-half-0 waves of the
+      // same queries through the stage the last block used
+      float* xch = reinterpret_cast<float*>(&tiles[buf ^ 1][0][0]) + qt * (DT * 16 * kWave);
+      if (kh == 1) {
+        if (SUM) {
+          xch[lane] = dl;
+        } else {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xch[(dt * 16 + i) * kWave + lane] = acc[dt][i];
+        }
+      }
+      __syncthreads();
+      if (kh == 0) {
+        if (SUM) {
+          dl += xch[lane];
+        } else {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[dt][i] += xch[(dt * 16 + i) * kWave + lane];
+        }
+      }
     }
+    const bool writer = qvalid && kh == 0;
+    if (SUM && writer && half == 0) delta_io[base + qi] = dl;
     // this item's q, dO, lse and D are no longer needed: the next item's load now
     if (has_next) load_rows(jn);
-    if (!SUM && qvalid) {
+    if (!SUM && writer) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -312,22 +351,22 @@ __device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, cons
 }
 
 // D pass: writes D_i for every query (FP32, [b*h*seq]).
-template <int D>
+template <int D, int QI>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_bwd_delta_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
     const uint4* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ delta, int seq, int heads,
     int qblocks, int bh_count, float scale2, AttnSlopes slopes) {
-  bwd_query_pass<D, true>(q, k, v, dout, lse, delta, nullptr, seq, heads, qblocks, bh_count, scale2, 1.f, slopes);
+  bwd_query_pass<D, true, QI>(q, k, v, dout, lse, delta, nullptr, seq, heads, qblocks, bh_count, scale2, 1.f, slopes);
 }
 
 // dq pass: dq_i = scale * sum_j ds_ij k_j with D_i from the D pass.
-template <int D>
+template <int D, int QI>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_bwd_dq_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
     const uint4* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ delta,
     uint2* __restrict__ dq, int seq, int heads, int qblocks, int bh_count, float scale2, float scale,
     AttnSlopes slopes) {
-  bwd_query_pass<D, false>(q, k, v, dout, lse, delta, dq, seq, heads, qblocks, bh_count, scale2, scale, slopes);
+  bwd_query_pass<D, false, QI>(q, k, v, dout, lse, delta, dq, seq, heads, qblocks, bh_count, scale2, scale, slopes);
 }
 
 // ---------------------------------------------------------------------------
@@ -509,19 +548,31 @@ void launch_bwd(const bloom_bf16* q, const bloom_bf16* k, const bloom_bf16* v, c
   const int bh_count = (int)(batch * heads);
   const int blocks = (int)((seq + kBwdBlock - 1) / kBwdBlock);
   const dim3 grid((unsigned)(bh_count * blocks));
-  // the D and dq kernels are persistent: two workgroups per compute unit, at most one per item
-  const int64_t n_items = (int64_t)bh_count * blocks;
+  // the D and dq kernels are persistent: two workgroups per compute unit, at
+  // most one per item.  Items of 128 queries while they fill two rounds of
+  // the grid, else of 64 (twice as many, so the causal work spreads evenly).
   const int64_t slots = 2 * (int64_t)(device_cu_count() > 0 ? device_cu_count() : 1);
+  const bool wide = (int64_t)bh_count * blocks >= 2 * slots;
+  const int qblocks = wide ? blocks : (int)((seq + 63) / 64);
+  const int64_t n_items = (int64_t)bh_count * qblocks;
   const dim3 grid_q((unsigned)(n_items < slots ? n_items : slots));
   const uint4* qv = reinterpret_cast<const uint4*>(q);
   const uint4* kv = reinterpret_cast<const uint4*>(k);
   const uint4* vv = reinterpret_cast<const uint4*>(v);
   const uint4* dov = reinterpret_cast<const uint4*>(dout);
-  hipLaunchKernelGGL((attention_bwd_delta_kernel<D>), grid_q, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov, lse,
-                     delta, (int)seq, (int)heads, blocks, bh_count, scale2, table);
-  hipLaunchKernelGGL((attention_bwd_dq_kernel<D>), grid_q, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov, lse,
-                     delta, reinterpret_cast<uint2*>(dq), (int)seq, (int)heads, blocks, bh_count, scale2, scale,
-                     table);
+  if (wide) {
+    hipLaunchKernelGGL((attention_bwd_delta_kernel<D, 128>), grid_q, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov,
+                       lse, delta, (int)seq, (int)heads, qblocks, bh_count, scale2, table);
+    hipLaunchKernelGGL((attention_bwd_dq_kernel<D, 128>), grid_q, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov, lse,
+                       delta, reinterpret_cast<uint2*>(dq), (int)seq, (int)heads, qblocks, bh_count, scale2, scale,
+                       table);
+  } else {
+    hipLaunchKernelGGL((attention_bwd_delta_kernel<D, 64>), grid_q, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov,
+                       lse, delta, (int)seq, (int)heads, qblocks, bh_count, scale2, table);
+    hipLaunchKernelGGL((attention_bwd_dq_kernel<D, 64>), grid_q, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov, lse,
+                       delta, reinterpret_cast<uint2*>(dq), (int)seq, (int)heads, qblocks, bh_count, scale2, scale,
+                       table);
+  }
   hipLaunchKernelGGL((attention_bwd_dkdv_kernel<D>), grid, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov, lse,
                      delta, reinterpret_cast<uint2*>(dk), reinterpret_cast<uint2*>(dv), (int)seq, (int)heads,
                      bh_count, scale2, scale, table);

@@ -92,7 +92,7 @@ def test_attention_bwd_workloads(wl):
 @pytest.mark.timeout(900)
 def test_attention_fwd_then_bwd_long_context_sampled():
     """The GPU forward's own lse feeds the backward: 2 of the 28 heads of the
-    8192-token extrapolation shape, sampled rows."""
+    8192-token extrapolation shape, sampled rows (64-query items)."""
     require_gpu()
     sm = W.LONG.softmax
     heads = 2
@@ -105,6 +105,34 @@ def test_attention_fwd_then_bwd_long_context_sampled():
     got = _bwd_gpu(q, k, v, do, tl.cpu().numpy(), sm.head_offset, sm.total_heads, sm.scale)
     rows = sample_rows(sm.seq, 16, W.LONG.seed, must=(0, 2047, 2048, sm.seq - 1))
     _check("long 8192", got, q, k, v, do, sm.head_offset, sm.total_heads, sm.scale, qrows=rows, krows=rows)
+
+
+def _wide_items(b, h, s):
+    """Whether the backward's D and dq kernels take items of 128 queries on
+    this GPU (else 64): when the 128-query items fill two rounds of two
+    workgroups per compute unit."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return b * h * ((s + 127) // 128) >= 4 * cus
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("b,h,s,d,seed", [(1, 64, 2048, 64, 61), (2, 64, 2048, 32, 62)])
+def test_attention_bwd_wide_items_sampled(b, h, s, d, seed):
+    """Shapes with many query blocks take the 128-query items (the other tests
+    take the 64-query ones): the GPU forward's lse feeds the backward, sampled
+    query and key rows against the oracle."""
+    require_gpu()
+    assert _wide_items(b, h, s), "shape no longer selects the 128-query items on this GPU"
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    q, k, v, do = _inputs(seed, b, h, s, d)
+    tq, tk, tv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    to = torch.empty_like(tq)
+    tl = torch.empty((b, h, s), dtype=torch.float32, device="cuda")
+    ops.bloom_alibi_attention_fwd(tq, tk, tv, to, tl, 0, 112, scale)
+    torch.cuda.synchronize()
+    got = _bwd_gpu(q, k, v, do, tl.cpu().numpy(), 0, 112, scale)
+    rows = sample_rows(s, 12, seed, must=(0, 63, 64, 127, 128, s - 1))
+    _check(f"wide {b}x{h}x{s}x{d}", got, q, k, v, do, 0, 112, scale, qrows=rows, krows=rows)
 
 
 @pytest.mark.timeout(900)
