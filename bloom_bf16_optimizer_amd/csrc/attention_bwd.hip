@@ -27,11 +27,12 @@
 //    rounding, 2^-9 of sum_d |dO_id o_id|, into every ds_ij of the row at
 //    weight p_ij; with ALiBi's steep slopes p is often near 1 on the diagonal
 //    and the error reaches the outputs.)
-//  * dk/dv: a workgroup takes 128 consecutive keys, a wave 32, and streams the
-//    query blocks (64 queries, Q and dO staged in LDS, with their lse and D)
-//    from its diagonal to the end.  It forms S = Q K^T and dP = dO V^T so that
-//    lane l owns key l%32, then dV^T += dO^T P and dK^T += Q^T dS with dO^T and
-//    Q^T read transposed from the staged tiles.
+//  * dk/dv: a workgroup of eight waves takes 128 consecutive keys, two waves
+//    per 32 keys, and streams the query blocks (64 queries, Q and dO staged in
+//    LDS, with their lse and D) from its diagonal to the end.  One wave of a
+//    pair forms S = Q K^T, P and dV^T += dO^T P; the other forms dP = dO V^T,
+//    takes P through LDS, and forms dS and dK^T += Q^T dS, with dO^T and Q^T
+//    read transposed from the staged tiles.  Lane l owns key l%32.
 // Products use v_mfma_f32_32x32x16_bf16 with FP32 accumulation.  P enters
 // as bf16 (it is >= 0, so its rounding stays relative to the result).  dS
 // enters dQ and dK as two bf16 parts, hi = bf16(ds) and lo = bf16(ds - hi),
@@ -65,8 +66,6 @@ struct BwdTile {
   static constexpr int RPB = 16 / CPR; // rows per 256 bytes
   static constexpr int Q4 = CPR / 4;
   static constexpr int CHUNKS = kBwdRows * CPR;
-  static constexpr int DMA = CHUNKS / kBwdThreads;  // transfers per lane per tile
-  static_assert(DMA >= 1 && CHUNKS % kBwdThreads == 0, "tile size");
   __device__ static int swz(int r) {
     const int x = r / RPB;
     return 4 * (x % Q4) + (x / Q4) % 4;
@@ -74,17 +73,22 @@ struct BwdTile {
 };
 
 // Requests rows [r0, r0+64) of a [seq, D] matrix (row index base + r) into
-// `tile`; wave w of the four moves chunks [64*(4x + w), +64) for each x.  Rows
-// past the end re-read row seq-1 (every use of them is masked).
-template <int D>
+// `tile`, moved by the first DW of the workgroup's NW waves: wave w < DW moves
+// chunks [64*(DW*x + w), +64) for each x.  Rows past the end re-read row
+// seq-1 (every use of them is masked).
+template <int D, int NW = 4>
 __device__ __forceinline__ void bwd_request(const uint4* __restrict__ g, attn_lds_uint4* tile, int64_t base, int r0,
                                            int seq, int w, int lane) {
   using T = BwdTile<D>;
+  constexpr int DW = T::CHUNKS / kWave < NW ? T::CHUNKS / kWave : NW;
+  constexpr int PER = T::CHUNKS / (DW * kWave);  // transfers per lane
+  static_assert(PER >= 1 && T::CHUNKS % (DW * kWave) == 0, "tile size");
+  if (w >= DW) return;  // wave-uniform
   const uint4* gb = attn_uniform(g + (base + r0) * T::CPR);
   const bool tail = r0 + kBwdRows > seq;  // wave-uniform
 #pragma unroll
-  for (int x = 0; x < T::DMA; ++x) {
-    const int first = (4 * x + w) * kWave;
+  for (int x = 0; x < PER; ++x) {
+    const int first = (DW * x + w) * kWave;
     const int slot = first + lane;
     const int r = slot / T::CPR, pc = slot % T::CPR;
     const int c = pc ^ T::swz(r);
@@ -370,38 +374,42 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 }
 
 // ---------------------------------------------------------------------------
-// dk/dv kernel: one 32-query tile (rows tr0 .. tr0+31 of the staged 64, global
-// queries qt0 ..) for one wave.  s, dp: rows = queries
-// qt0 + 8*(i/4) + 4*half + i%4, column = this lane's key kj.  MASK: some key
-// of the wave is after some query of the tile, or the tile runs past seq.
+// dk/dv kernel.  A workgroup of eight waves takes 128 consecutive keys of one
+// (b, h): waves w and w+4 own keys 32*(w%4) .. +31.  Wave w (the P wave) forms
+// S = Q K^T and P for them and accumulates dV; wave w+4 (the dS wave) forms
+// dP = dO V^T, takes P from the P wave through LDS, forms dS and accumulates
+// dK.  Neither holds both accumulators, so two waves fit on a SIMD, and S is
+// formed once.  Both stream the query blocks (64 queries, Q and dO staged in
+// LDS with their lse and D) from the diagonal to the end, 32 queries (one
+// tile) at a time, in two phases per block with a barrier between them:
+//   phase 1: P waves S, P (stored to LDS) | dS waves dP
+//   phase 2: P waves dV^T += dO^T P      | dS waves dS, dK^T += Q^T dS
+// so that each SIMD runs one wave's products against the other's vector
+// work.  s, dp, p: rows = queries qt0 + 8*(i/4) + 4*half + i%4, column = this
+// lane's key kj.  MASK: some key of the wave is after some query of the
+// tile, or the tile runs past seq.
+
+// P wave, phase 1: S = Q K^T and p = exp2(s*scale2 + bias - lse2) for one
+// tile (rows tr0 .. tr0+31 of the staged 64, global queries qt0 ..); p goes
+// to LDS as FP32 and into pf as bf16.
 template <int D, bool MASK>
-__device__ __forceinline__ void dkdv_tile(f32x16_t (&dkacc)[D / 32], f32x16_t (&dvacc)[D / 32],
-                                          const attn_lds_uint4* __restrict__ q_lds,
-                                          const attn_lds_uint4* __restrict__ do_lds, const float4* lse_lds,
-                                          const float4* delta_lds, const bf16x8_t (&kf)[D / 16],
-                                          const bf16x8_t (&vf)[D / 16], float scale2, float slope2, int kj, int tr0,
-                                          int qt0, int seq, int half, int col, int lane) {
+__device__ __forceinline__ void p_tile(bf16x8_t (&pf)[2], float4* __restrict__ pout, const attn_lds_uint4* __restrict__ q_lds,
+                                       const float4* lse_lds, const bf16x8_t (&kf)[D / 16], float scale2, float slope2,
+                                       int kj, int tr0, int qt0, int seq, int half, int col, int lane) {
   using T = BwdTile<D>;
-  constexpr int KS = D / 16, DT = D / 32;
-  const f32x16_t zero = {};
-  f32x16_t s = zero, dp = zero;
+  constexpr int KS = D / 16;
+  f32x16_t s = {};
   const int sw = T::swz(tr0 + col);
   const attn_lds_u32x4* qr = reinterpret_cast<const attn_lds_u32x4*>(q_lds) + (tr0 + col) * T::CPR;
-  const attn_lds_u32x4* dr = reinterpret_cast<const attn_lds_u32x4*>(do_lds) + (tr0 + col) * T::CPR;
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    const int c = (2 * kk + half) ^ sw;
-    s = mfma32(__builtin_bit_cast(bf16x8_t, qr[c]), kf[kk], s);
-    dp = mfma32(__builtin_bit_cast(bf16x8_t, dr[c]), vf[kk], dp);
-  }
+  for (int kk = 0; kk < KS; ++kk) s = mfma32(__builtin_bit_cast(bf16x8_t, qr[(2 * kk + half) ^ sw]), kf[kk], s);
   // base-2 logit minus lse: s*scale2 + slope2*(kj - query) - lse2(query)
   const float cb = slope2 * (float)(kj - qt0 - 4 * half);
-  bf16x8_t pf[2], dsh[2], dsl[2];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const float4 l4 = lse_lds[(tr0 + 8 * g + 4 * half) / 4];
-    const float4 d4 = delta_lds[(tr0 + 8 * g + 4 * half) / 4];
-    const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+    float p4[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 4 * g + r;
@@ -411,130 +419,263 @@ __device__ __forceinline__ void dkdv_tile(f32x16_t (&dkacc)[D / 32], f32x16_t (&
         const int qq = qt0 + 4 * half + qoff;
         if (kj > qq || qq >= seq) p = 0.f;
       }
+      p4[r] = p;
       pf[i / 8][i % 8] = (__bf16)p;
-      const Bf16Pair d2 = split_bf16(p * (dp[i] - dv4[r]));
-      dsh[i / 8][i % 8] = d2.hi;
-      dsl[i / 8][i % 8] = d2.lo;
     }
+    pout[g * kWave + lane] = make_float4(p4[0], p4[1], p4[2], p4[3]);
   }
-  // dV^T += dO^T P and dK^T += Q^T dS over the tile's 2 query steps
+}
+
+// P wave, phase 2: dV^T += dO^T P over the tile's 2 query steps.
+template <int D>
+__device__ __forceinline__ void dv_tile(f32x16_t (&dvacc)[D / 32], const bf16x8_t (&pf)[2],
+                                        const attn_lds_uint4* __restrict__ do_lds, int tr0, int half, int lane) {
+  using T = BwdTile<D>;
+  constexpr int DT = D / 32;
   const int tj = (lane & 15) >> 2, tc = lane & 3, tg = (lane >> 4) & 1;
   const int trow = 4 * half + tj;
   const int sw0 = T::swz(trow), sw8 = T::swz(trow + 8);  // unchanged by row offsets that are multiples of 16
-  const char __attribute__((address_space(3)))* qbytes =
-      reinterpret_cast<const char __attribute__((address_space(3)))*>(q_lds);
   const char __attribute__((address_space(3)))* dbytes =
       reinterpret_cast<const char __attribute__((address_space(3)))*>(do_lds);
 #pragma unroll
   for (int stp = 0; stp < 2; ++stp)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int dt = 0; dt < DT; ++dt)
       dvacc[dt] = mfma32(bwd_read_tr<D>(dbytes, tr0 + 16 * stp, dt, trow, tg, tc, sw0, sw8), pf[stp], dvacc[dt]);
+}
+
+// dS wave, phase 1: dP = dO V^T for one tile.
+template <int D>
+__device__ __forceinline__ f32x16_t dp_tile(const attn_lds_uint4* __restrict__ do_lds, const bf16x8_t (&vf)[D / 16],
+                                            int tr0, int half, int col) {
+  using T = BwdTile<D>;
+  constexpr int KS = D / 16;
+  f32x16_t dp = {};
+  const int sw = T::swz(tr0 + col);
+  const attn_lds_u32x4* dr = reinterpret_cast<const attn_lds_u32x4*>(do_lds) + (tr0 + col) * T::CPR;
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) dp = mfma32(__builtin_bit_cast(bf16x8_t, dr[(2 * kk + half) ^ sw]), vf[kk], dp);
+  return dp;
+}
+
+// dS wave, phase 2: dS = P (dP - D) in two bf16 parts, dK^T += Q^T dS over
+// the tile's 2 query steps.
+template <int D>
+__device__ __forceinline__ void dk_tile(f32x16_t (&dkacc)[D / 32], const f32x16_t& dp, const float4* __restrict__ pin,
+                                        const attn_lds_uint4* __restrict__ q_lds, const float4* delta_lds, int tr0,
+                                        int half, int lane) {
+  using T = BwdTile<D>;
+  constexpr int DT = D / 32;
+  bf16x8_t dsh[2], dsl[2];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const float4 p4 = pin[g * kWave + lane];
+    const float4 d4 = delta_lds[(tr0 + 8 * g + 4 * half) / 4];
+    const float pv[4] = {p4.x, p4.y, p4.z, p4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * g + r;
+      const Bf16Pair d2 = split_bf16(pv[r] * (dp[i] - dv4[r]));
+      dsh[i / 8][i % 8] = d2.hi;
+      dsl[i / 8][i % 8] = d2.lo;
+    }
+  }
+  const int tj = (lane & 15) >> 2, tc = lane & 3, tg = (lane >> 4) & 1;
+  const int trow = 4 * half + tj;
+  const int sw0 = T::swz(trow), sw8 = T::swz(trow + 8);
+  const char __attribute__((address_space(3)))* qbytes =
+      reinterpret_cast<const char __attribute__((address_space(3)))*>(q_lds);
+#pragma unroll
+  for (int stp = 0; stp < 2; ++stp)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
       const bf16x8_t qT = bwd_read_tr<D>(qbytes, tr0 + 16 * stp, dt, trow, tg, tc, sw0, sw8);
       dkacc[dt] = mfma32(qT, dsh[stp], dkacc[dt]);
       dkacc[dt] = mfma32(qT, dsl[stp], dkacc[dt]);
     }
 }
 
+constexpr int kKvWaves = 8;
+constexpr int kKvThreads = kKvWaves * kWave;
+
 template <int D>
-__global__ __launch_bounds__(kBwdThreads) void attention_bwd_dkdv_kernel(
-    const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
-    const uint4* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    uint2* __restrict__ dk, uint2* __restrict__ dv, int seq, int heads, int bh_count, float scale2, float scale,
-    AttnSlopes slopes) {
+struct KvShared {
+  uint4 tiles[2][2][BwdTile<D>::CHUNKS];  // [stage][Q, dO]
+  float4 rowv[2][2][kBwdRows / 4];        // [stage][lse2, D] of the 64 queries
+  float4 pbuf[2][4][4 * kWave];           // [tile][key group]: P, 16 values per lane
+};
+
+// One role's walk over the workgroup's items (DSW: the dS waves).  The two
+// roles run the same sequence of barriers; every other step differs, so the
+// role is a template parameter and each role's registers are allocated alone.
+//
+// Persistent workgroups, one per compute unit: a workgroup takes items (128
+// keys of one (b, h), numbered longest first: item j is key block j/bh_count
+// of (b, h) = j % bh_count) in a snake over the grid, as the query-side
+// kernels do.  The next block (or the next item's first block) is in flight
+// while a block is used.
+template <int D, bool DSW>
+__device__ __forceinline__ void dkdv_walk(KvShared<D>& sh, const uint4* __restrict__ q, const uint4* __restrict__ k,
+                                          const uint4* __restrict__ v, const uint4* __restrict__ dout,
+                                          const float* __restrict__ lse, const float* __restrict__ delta,
+                                          uint2* __restrict__ out, int seq, int heads, int kblocks, int bh_count,
+                                          float scale2, float outscale, const AttnSlopes& slopes) {
   constexpr int KS = D / 16, DT = D / 32, VPR = D / 8;
   constexpr int CH = BwdTile<D>::CHUNKS;
-  __shared__ __attribute__((aligned(16))) uint4 tiles[2][2][CH];        // [stage][Q, dO]
-  __shared__ float4 rowv[2][2][kBwdRows / 4];                           // [stage][lse2, D] of the 64 queries
-
   const int t = threadIdx.x;
   const int w = t / kWave, lane = t & (kWave - 1), half = lane >> 5, col = lane & 31;
-  // the longest workgroups (first key blocks) first
-  const int kb = (int)(blockIdx.x / (unsigned)bh_count);
-  const int64_t bh = blockIdx.x % (unsigned)bh_count;
-  const int h = (int)(bh % heads);
-  const float slope2 = slopes.s[h];
-  const int64_t base = bh * (int64_t)seq;
-  const int kw0 = kb * kBwdBlock + w * 32;  // this wave's first key
-  const int kj = kw0 + col;
-  const bool kvalid = kj < seq;
-  const bool wave_live = kw0 < seq;
+  const int kgrp = w % 4;  // this wave's 32 keys within the item
+  attn_lds_uint4* lt = (attn_lds_uint4*)&sh.tiles[0][0][0];
+  auto tile = [&](int stage, int which) { return lt + (stage * 2 + which) * CH; };
 
-  // B operands: this lane's key row of k and v (d = 16*kk + 8*half .. +8)
-  bf16x8_t kf[KS], vf[KS];
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
-    const int64_t idx = (base + kj) * VPR + 2 * kk + half;
-    kf[kk] = as_bf16x8(kvalid ? k[idx] : z4);
-    vf[kk] = as_bf16x8(kvalid ? v[idx] : z4);
-  }
-  f32x16_t dkacc[DT], dvacc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dkacc[dt][i] = dvacc[dt][i] = 0.f;
+  const int G = (int)gridDim.x, g = (int)blockIdx.x;
+  const int n_items = kblocks * bh_count;
+  auto item_j = [&](int r) { return r * G + ((r & 1) ? G - 1 - g : g); };
+  const int nqb = (seq + kBwdRows - 1) / kBwdRows;
 
-  // Row values of a query block: lanes 0..15 of wave 0 move 4 lse values
-  // each, lanes 16..31 4 values of D (groups past seq re-read the last group;
-  // seq is a multiple of 8, so a group of 4 is wholly inside or outside).
-  auto row_load = [&](int r0) {
+  int j = item_j(0);
+  if (j >= n_items) return;  // uniform over the workgroup
+
+  // B operand: this lane's key row of k (P waves) or v (dS waves),
+  // d = 16*kk + 8*half .. +8; keys past seq read row seq-1 and are zeroed
+  bf16x8_t kv[KS];
+  auto load_keys = [&](int jn) {
+    const int kj_ = (jn / bh_count) * kBwdBlock + kgrp * 32 + col;
+    const bool ok = kj_ < seq;
+    const int64_t row = (int64_t)(jn % bh_count) * seq + min(kj_, seq - 1);
+    const uint4* src = DSW ? v : k;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint4 a = src[row * VPR + 2 * kk + half];
+      kv[kk] = as_bf16x8(ok ? a : make_uint4(0u, 0u, 0u, 0u));
+    }
+  };
+  // Row values of a query block: lanes 0..15 of wave 0 (a P wave) move 4 lse
+  // values each, lanes 16..31 4 values of D (groups past seq re-read the last
+  // group; seq is a multiple of 8, so a group of 4 is wholly inside or outside).
+  auto row_load = [&](int64_t base_, int r0) {
     const int grp = r0 + 4 * (t & 15);
-    const int64_t at = base + min(grp, seq - 4);
+    const int64_t at = base_ + min(grp, seq - 4);
     return (t < 16) ? *reinterpret_cast<const float4*>(lse + at) : *reinterpret_cast<const float4*>(delta + at);
   };
   auto row_store = [&](int stage, float4 x) {
     if (t < 16) x = make_float4(x.x * kLog2e, x.y * kLog2e, x.z * kLog2e, x.w * kLog2e);
-    rowv[stage][t >> 4][t & 15] = x;
+    sh.rowv[stage][t >> 4][t & 15] = x;
   };
+  auto request_block = [&](int64_t base_, int qb_, int stage) {
+    bwd_request<D, kKvWaves>(q, tile(stage, 0), base_, qb_ * kBwdRows, seq, w, lane);
+    bwd_request<D, kKvWaves>(dout, tile(stage, 1), base_, qb_ * kBwdRows, seq, w, lane);
+  };
+  auto first_qb = [&](int jn) { return ((jn / bh_count) * kBwdBlock) / kBwdRows; };  // block of the item's first key
 
-  const int nqb = (seq + kBwdRows - 1) / kBwdRows;
-  int qbi = (kb * kBwdBlock) / kBwdRows;  // the block holding this workgroup's first key
-  attn_lds_uint4* lt = (attn_lds_uint4*)&tiles[0][0][0];
-  auto tile = [&](int stage, int which) { return lt + (stage * 2 + which) * CH; };
-  bwd_request<D>(q, tile(0, 0), base, qbi * kBwdRows, seq, w, lane);
-  bwd_request<D>(dout, tile(0, 1), base, qbi * kBwdRows, seq, w, lane);
-  if (t < 32) row_store(0, row_load(qbi * kBwdRows));
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int buf = 0; qbi < nqb; ++qbi, buf ^= 1) {
-    const int q0 = qbi * kBwdRows;
-    const bool next = qbi + 1 < nqb;
-    float4 rv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (next) {
-      bwd_request<D>(q, tile(buf ^ 1, 0), base, q0 + kBwdRows, seq, w, lane);
-      bwd_request<D>(dout, tile(buf ^ 1, 1), base, q0 + kBwdRows, seq, w, lane);
-      if (t < 32) rv = row_load(q0 + kBwdRows);
-    }
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int qt0 = q0 + 32 * tt;
-      if (wave_live && qt0 < seq && kw0 <= qt0 + 31) {
-        if (kw0 + 31 > qt0 || qt0 + 32 > seq)
-          dkdv_tile<D, true>(dkacc, dvacc, tile(buf, 0), tile(buf, 1), rowv[buf][0], rowv[buf][1], kf, vf, scale2,
-                             slope2, kj, 32 * tt, qt0, seq, half, col, lane);
-        else
-          dkdv_tile<D, false>(dkacc, dvacc, tile(buf, 0), tile(buf, 1), rowv[buf][0], rowv[buf][1], kf, vf, scale2,
-                              slope2, kj, 32 * tt, qt0, seq, half, col, lane);
-      }
-    }
-    if (next && t < 32) row_store(buf ^ 1, rv);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  load_keys(j);
+  {
+    const int64_t base0 = (int64_t)(j % bh_count) * seq;
+    request_block(base0, first_qb(j), 0);
+    if (!DSW && t < 32) row_store(0, row_load(base0, first_qb(j) * kBwdRows));
   }
-  if (kvalid) {
+  int buf = 0;  // the stage holding the next block to use
+  for (int r = 0;; ++r) {
+    const int kb = j / bh_count;
+    const int64_t bh = j % bh_count;
+    const int h = (int)(bh % heads);
+    const float slope2 = slopes.s[h];
+    const int64_t base = bh * (int64_t)seq;
+    const int kw0 = kb * kBwdBlock + kgrp * 32;  // this wave's first key
+    const int kj = kw0 + col;
+    const bool kvalid = kj < seq;
+    const bool wave_live = kw0 < seq;
+    const int jn = item_j(r + 1);
+    const bool has_next = jn < n_items;
+
+    f32x16_t acc[DT];  // dK^T (dS waves) or dV^T (P waves) of this wave's keys
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // d = 32*dt + 8*g + 4*half + 0..3
-        const int64_t at = (base + kj) * (D / 4) + (32 * dt + 8 * g + 4 * half) / 4;
-        dk[at] = make_uint2(pack2(dkacc[dt][4 * g] * scale, dkacc[dt][4 * g + 1] * scale),
-                            pack2(dkacc[dt][4 * g + 2] * scale, dkacc[dt][4 * g + 3] * scale));
-        dv[at] = make_uint2(pack2(dvacc[dt][4 * g], dvacc[dt][4 * g + 1]),
-                            pack2(dvacc[dt][4 * g + 2], dvacc[dt][4 * g + 3]));
+      for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int qbi = first_qb(j); qbi < nqb; ++qbi, buf ^= 1) {
+      const int q0 = qbi * kBwdRows;
+      const bool next = qbi + 1 < nqb;
+      float4 rv = make_float4(0.f, 0.f, 0.f, 0.f);
+      // the next block arrives while this one is used (the barrier that
+      // ended the previous iteration freed its buffer)
+      if (next) {
+        request_block(base, qbi + 1, buf ^ 1);
+        if (!DSW && t < 32) rv = row_load(base, q0 + kBwdRows);
+      } else if (has_next) {
+        const int64_t bn = (int64_t)(jn % bh_count) * seq;
+        request_block(bn, first_qb(jn), buf ^ 1);
+        if (!DSW && t < 32) rv = row_load(bn, first_qb(jn) * kBwdRows);
       }
+      bool live[2], mask[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int qt0 = q0 + 32 * tt;
+        live[tt] = wave_live && qt0 < seq && kw0 <= qt0 + 31;
+        mask[tt] = kw0 + 31 > qt0 || qt0 + 32 > seq;
+      }
+      if constexpr (DSW) {
+        f32x16_t dpt[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          if (live[tt]) dpt[tt] = dp_tile<D>(tile(buf, 1), kv, 32 * tt, half, col);
+        __syncthreads();  // the P waves' P of this block is in LDS
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          if (live[tt]) dk_tile<D>(acc, dpt[tt], sh.pbuf[tt][kgrp], tile(buf, 0), sh.rowv[buf][1], 32 * tt, half, lane);
+      } else {
+        bf16x8_t pf[2][2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          if (!live[tt]) continue;
+          if (mask[tt])
+            p_tile<D, true>(pf[tt], sh.pbuf[tt][kgrp], tile(buf, 0), sh.rowv[buf][0], kv, scale2, slope2, kj,
+                            32 * tt, q0 + 32 * tt, seq, half, col, lane);
+          else
+            p_tile<D, false>(pf[tt], sh.pbuf[tt][kgrp], tile(buf, 0), sh.rowv[buf][0], kv, scale2, slope2, kj,
+                             32 * tt, q0 + 32 * tt, seq, half, col, lane);
+        }
+        __syncthreads();  // P is in LDS for the dS waves
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          if (live[tt]) dv_tile<D>(acc, pf[tt], tile(buf, 1), 32 * tt, half, lane);
+        if ((next || has_next) && t < 32) row_store(buf ^ 1, rv);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    // this item's key rows are no longer needed: the next item's load now
+    if (has_next) load_keys(jn);
+    if (kvalid) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          // d = 32*dt + 8*gg + 4*half + 0..3
+          const int64_t at = (base + kj) * (D / 4) + (32 * dt + 8 * gg + 4 * half) / 4;
+          out[at] = make_uint2(pack2(acc[dt][4 * gg] * outscale, acc[dt][4 * gg + 1] * outscale),
+                               pack2(acc[dt][4 * gg + 2] * outscale, acc[dt][4 * gg + 3] * outscale));
+        }
+    }
+    if (!has_next) break;  // uniform over the workgroup
+    j = jn;
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_bwd_dkdv_kernel(
+    const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
+    const uint4* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    uint2* __restrict__ dk, uint2* __restrict__ dv, int seq, int heads, int kblocks, int bh_count, float scale2,
+    float scale, AttnSlopes slopes) {
+  __shared__ __attribute__((aligned(16))) KvShared<D> sh;
+  if (threadIdx.x >= 4 * kWave)  // wave-uniform: waves 4..7 are the dS waves
+    dkdv_walk<D, true>(sh, q, k, v, dout, lse, delta, dk, seq, heads, kblocks, bh_count, scale2, scale, slopes);
+  else
+    dkdv_walk<D, false>(sh, q, k, v, dout, lse, delta, dv, seq, heads, kblocks, bh_count, scale2, 1.f, slopes);
 }
 
 size_t bwd_workspace(int64_t batch, int32_t heads, int64_t seq) {
@@ -547,7 +688,6 @@ void launch_bwd(const bloom_bf16* q, const bloom_bf16* k, const bloom_bf16* v, c
                 const AttnSlopes& table, hipStream_t stream) {
   const int bh_count = (int)(batch * heads);
   const int blocks = (int)((seq + kBwdBlock - 1) / kBwdBlock);
-  const dim3 grid((unsigned)(bh_count * blocks));
   // the D and dq kernels are persistent: two workgroups per compute unit, at
   // most one per item.  Items of 128 queries while they fill two rounds of
   // the grid, else of 64 (twice as many, so the causal work spreads evenly).
@@ -573,8 +713,12 @@ void launch_bwd(const bloom_bf16* q, const bloom_bf16* k, const bloom_bf16* v, c
                        delta, reinterpret_cast<uint2*>(dq), (int)seq, (int)heads, qblocks, bh_count, scale2, scale,
                        table);
   }
-  hipLaunchKernelGGL((attention_bwd_dkdv_kernel<D>), grid, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov, lse,
-                     delta, reinterpret_cast<uint2*>(dk), reinterpret_cast<uint2*>(dv), (int)seq, (int)heads,
+  // the dk/dv kernel is persistent too: one eight-wave workgroup per compute unit
+  const int64_t kv_items = (int64_t)bh_count * blocks;
+  const int64_t cus = slots / 2;
+  const dim3 grid_kv((unsigned)(kv_items < cus ? kv_items : cus));
+  hipLaunchKernelGGL((attention_bwd_dkdv_kernel<D>), grid_kv, dim3(kKvThreads), 0, stream, qv, kv, vv, dov, lse,
+                     delta, reinterpret_cast<uint2*>(dk), reinterpret_cast<uint2*>(dv), (int)seq, (int)heads, blocks,
                      bh_count, scale2, scale, table);
 }
 
