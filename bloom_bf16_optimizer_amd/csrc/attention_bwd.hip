@@ -385,7 +385,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 //   phase 1: P waves S, P (stored to LDS) | dS waves dP
 //   phase 2: P waves dV^T += dO^T P      | dS waves dS, dK^T += Q^T dS
 // so that each SIMD runs one wave's products against the other's vector
-// work.  s, dp, p: rows = queries qt0 + 8*(i/4) + 4*half + i%4, column = this
+// work; within a block the P waves run one 32-query tile ahead (three phases,
+// see the walk below).  s, dp, p: rows = queries qt0 + 8*(i/4) + 4*half + i%4, column = this
 // lane's key kj.  MASK: some key of the wave is after some query of the
 // tile, or the tile runs past seq.
 
@@ -617,31 +618,37 @@ __device__ __forceinline__ void dkdv_walk(KvShared<D>& sh, const uint4* __restri
         live[tt] = wave_live && qt0 < seq && kw0 <= qt0 + 31;
         mask[tt] = kw0 + 31 > qt0 || qt0 + 32 > seq;
       }
+      // three phases, one barrier between each: the P waves run one tile
+      // ahead of the dS waves
+      //   A: P waves S, P of tile 0           | dS waves dP of tiles 0 and 1
+      //   B: P waves S, P of tile 1; dV tile 0 | dS waves dS, dK of tile 0
+      //   C: P waves dV of tile 1             | dS waves dS, dK of tile 1
       if constexpr (DSW) {
         f32x16_t dpt[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
           if (live[tt]) dpt[tt] = dp_tile<D>(tile(buf, 1), kv, 32 * tt, half, col);
-        __syncthreads();  // the P waves' P of this block is in LDS
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt) {
+          __syncthreads();  // the P waves' P of tile tt is in LDS
           if (live[tt]) dk_tile<D>(acc, dpt[tt], sh.pbuf[tt][kgrp], tile(buf, 0), sh.rowv[buf][1], 32 * tt, half, lane);
+        }
       } else {
         bf16x8_t pf[2][2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          if (!live[tt]) continue;
-          if (mask[tt])
-            p_tile<D, true>(pf[tt], sh.pbuf[tt][kgrp], tile(buf, 0), sh.rowv[buf][0], kv, scale2, slope2, kj,
-                            32 * tt, q0 + 32 * tt, seq, half, col, lane);
-          else
-            p_tile<D, false>(pf[tt], sh.pbuf[tt][kgrp], tile(buf, 0), sh.rowv[buf][0], kv, scale2, slope2, kj,
-                             32 * tt, q0 + 32 * tt, seq, half, col, lane);
+          if (live[tt]) {
+            if (mask[tt])
+              p_tile<D, true>(pf[tt], sh.pbuf[tt][kgrp], tile(buf, 0), sh.rowv[buf][0], kv, scale2, slope2, kj,
+                              32 * tt, q0 + 32 * tt, seq, half, col, lane);
+            else
+              p_tile<D, false>(pf[tt], sh.pbuf[tt][kgrp], tile(buf, 0), sh.rowv[buf][0], kv, scale2, slope2, kj,
+                               32 * tt, q0 + 32 * tt, seq, half, col, lane);
+          }
+          if (tt == 1 && live[0]) dv_tile<D>(acc, pf[0], tile(buf, 1), 0, half, lane);
+          __syncthreads();  // P of tile tt is in LDS for the dS waves
         }
-        __syncthreads();  // P is in LDS for the dS waves
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-          if (live[tt]) dv_tile<D>(acc, pf[tt], tile(buf, 1), 32 * tt, half, lane);
+        if (live[1]) dv_tile<D>(acc, pf[1], tile(buf, 1), 32, half, lane);
         if ((next || has_next) && t < 32) row_store(buf ^ 1, rv);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
