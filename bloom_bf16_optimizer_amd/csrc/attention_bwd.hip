@@ -49,7 +49,7 @@ namespace {
 
 constexpr int kBwdThreads = 256;  // four waves
 constexpr int kBwdRows = 64;      // rows of a staged tile (keys for dq, queries for dk/dv)
-constexpr int kBwdBlock = 128;    // queries (dq) or keys (dk/dv) per workgroup, 32 per wave
+constexpr int kBwdBlock = 128;    // keys per dk/dv item; queries per D/dq item (or 64, see the launcher)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // One staged tile: 64 rows of D bf16, row-major, written straight from global
