@@ -109,7 +109,7 @@ constexpr float kAttnLazyMax = 8.0f;
 //   t = S*scale2 + slope2*(k0 - q),
 // the second term being one number per lane per block.  DIAG: some key of
 // the block is after some query of the wave, so the causal mask applies.
-template <int D, bool DIAG>
+template <int D, bool DIAG, bool OPT = false>
 __device__ __forceinline__ void attn_block(AttnState<D>& st, const attn_lds_uint4* __restrict__ kt_lds,
                                            const attn_lds_uint4* __restrict__ vt_lds, const bf16x8_t (&qf)[D / 16],
                                            const bf16x8_t (&kx)[2], const bf16x8_t& qx, float scale2,
@@ -139,36 +139,62 @@ __device__ __forceinline__ void attn_block(AttnState<D>& st, const attn_lds_uint
       for (int i = 0; i < 16; ++i)
         if (k0 + 32 * kt + 8 * (i / 4) + 4 * half + (i % 4) > qi) s[kt][i] = -INFINITY;
   }
-  // Row max: scale2 > 0, so the max of S*scale2 is scale2 times the max of S.
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-  const float shift = slope2 * (float)(k0 - qi);
-  float bm = fmaf(mx, scale2, shift);
-  bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
-  if (__ballot(bm > st.m + kAttnLazyMax) != 0) {  // wave-uniform: rescale to a new max
-    const float m_new = fmaxf(st.m, bm);
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);  // 0 on the first block
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st.oacc[dt][i] *= alpha;
-    st.l *= alpha;
-    st.m = m_new;
-  }
-  const float c = fmaf(slope2, (float)(k0 - qi), -st.m);
   bf16x8_t pf[4];
-  float l = st.l;
+  // The block's row max and a rescale when it exceeds the running max by
+  // more than kAttnLazyMax (true if it rescaled).
+  auto exact = [&]() {
+    // Row max: scale2 > 0, so the max of S*scale2 is scale2 times the max of S.
+    float mx = -INFINITY;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], scale2, c));
-      l += p;
-      pf[2 * kt + i / 8][i % 8] = (__bf16)p;
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+    const float shift = slope2 * (float)(k0 - qi);
+    float bm = fmaf(mx, scale2, shift);
+    bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+    if (__ballot(bm > st.m + kAttnLazyMax) != 0) {  // wave-uniform: rescale to a new max
+      const float m_new = fmaxf(st.m, bm);
+      const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);  // 0 on the first block
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.oacc[dt][i] *= alpha;
+      st.l *= alpha;
+      st.m = m_new;
+      return true;
     }
+    return false;
+  };
+  // The block's weights against the running max, into pf; returns the
+  // running sum with them added.
+  auto weights = [&]() {
+    const float c = fmaf(slope2, (float)(k0 - qi), -st.m);
+    float l = st.l;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][i], scale2, c));
+        l += p;
+        pf[2 * kt + i / 8][i % 8] = (__bf16)p;
+      }
+    return l;
+  };
+  float l;
+  if (DIAG || !OPT) {
+    exact();
+    l = weights();
+  } else {
+    // OPT (callers whose waves reach every off-diagonal block after their
+    // diagonal one, so the running max is set): away from the diagonal the
+    // ALiBi bias keeps the logits below the running max, so the weights are
+    // formed against it directly.  If a lane's block sum passes 2^7 (every
+    // weight above 2^8 does), the block is redone the exact way; where that
+    // way would not rescale, its weights are these ones.  Either way the
+    // result is the exact way's.
+    l = weights();
+    if (__ballot(!(l - st.l <= 128.f)) != 0 && exact()) l = weights();
+  }
   st.l = l;
   // O^T += V^T P^T over the 4 key steps of the block; the k order of step
   // stp is keys 16*stp + 4*half + {0..3, 8..11} for lane half `half`.  The
@@ -481,7 +507,8 @@ __global__ __launch_bounds__(kAttnGroupThreads) __attribute__((amdgpu_waves_per_
       if (k0 + kAttnBlockN - 1 > q0)
         attn_block<D, true>(st, tile(buf, 0), tile(buf, 1), qf, kx, qx, scale2, slope2, k0, qi, half, col, lane);
       else
-        attn_block<D, false>(st, tile(buf, 0), tile(buf, 1), qf, kx, qx, scale2, slope2, k0, qi, half, col, lane);
+        attn_block<D, false, true>(st, tile(buf, 0), tile(buf, 1), qf, kx, qx, scale2, slope2, k0, qi, half, col,
+                                   lane);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
