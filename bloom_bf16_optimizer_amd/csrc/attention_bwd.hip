@@ -10,19 +10,20 @@
 //   dq_i  = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
 //   dv_j  = sum_i p_ij dO_i.
 //
-// Three kernels, each owning its outputs (no atomics, results independent of
+// Two kernels, each owning its outputs (no atomics, results independent of
 // scheduling):
-//  * D and dq: two kernels with one body.  A workgroup of four waves takes
-//    128 consecutive queries of one (b, h), a wave 32 (or, in launches with
-//    few query blocks, 64 queries, a wave 32 of them against half the keys),
-//    and streams the key blocks (64 keys, K and V staged in LDS) up to its
-//    diagonal once.  Both
-//    form S^T = K Q^T and dP^T = V dO^T so that lane l owns query l%32 (its
-//    lse and D_i are one number each).  The D kernel sums
-//    D_i = sum_j p_ij dp_ij in FP32 and writes it to the workspace; the dq
-//    kernel reads it back, forms dS and dQ^T += K^T dS^T with K^T read from
-//    the same LDS tile by the transposing ds_read_b64_tr_b16.  Apart, each
-//    fits the 256 registers that let two waves share a SIMD.
+//  * query side (D and dq): a workgroup of four waves takes 128 consecutive
+//    queries of one (b, h), a wave 32 (or, in launches with few query
+//    blocks, 64 queries, a wave 32 of them against half the keys), and
+//    streams the key blocks (64 keys, K and V staged in LDS) up to its
+//    diagonal twice.  Both passes form S^T = K Q^T and dP^T = V dO^T so that
+//    lane l owns query l%32 (its lse and D_i are one number each).  The first
+//    sums D_i = sum_j p_ij dp_ij in FP32 and writes it to the workspace for
+//    the dk/dv kernel; the second forms dS with that D and dQ^T += K^T dS^T
+//    with K^T read from the same LDS tile by the transposing
+//    ds_read_b64_tr_b16.  Each pass takes a block's 32-key halves one at a
+//    time, so the kernel fits the 256 registers that let two waves share a
+//    SIMD.
 //    (The usual shortcut D_i = dO_i . o_i from the stored bf16 o carries that
 //    rounding, 2^-9 of sum_d |dO_id o_id|, into every ds_ij of the row at
 //    weight p_ij; with ALiBi's steep slopes p is often near 1 on the diagonal
@@ -41,6 +42,7 @@
 // rounding of ds (2^-9 of each term) would show in the result.  The
 // exponentials are base 2 (scale, slopes and lse pre-multiplied by log2 e).
 #include <cmath>
+#include <type_traits>
 
 #include "attention_common.h"
 
@@ -49,7 +51,7 @@ namespace {
 
 constexpr int kBwdThreads = 256;  // four waves
 constexpr int kBwdRows = 64;      // rows of a staged tile (keys for dq, queries for dk/dv)
-constexpr int kBwdBlock = 128;    // keys per dk/dv item; queries per D/dq item (or 64, see the launcher)
+constexpr int kBwdBlock = 128;    // keys per dk/dv item; queries per query-side item (or 64, see the launcher)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // One staged tile: 64 rows of D bf16, row-major, written straight from global
@@ -186,27 +188,29 @@ __device__ __forceinline__ void dq_block(f32x16_t (&acc)[D / 32], float& dsum, c
   }
 }
 
-// The two query-side kernels share one body: a workgroup of four waves takes
-// items of QI consecutive queries of one (b, h) and streams the key blocks
-// (64 keys, K and V staged in LDS) from its diagonal down to key 0 once.
+// The query-side kernel: a workgroup of four waves takes items of QI
+// consecutive queries of one (b, h) and streams the key blocks (64 keys, K
+// and V staged in LDS) from its diagonal down to key 0 twice: the D pass
+// sums D_i = sum_j p_ij dp_ij for its queries (and writes it to `delta_out`
+// for the dk/dv kernel), then the dq pass forms dS with that D, still in
+// registers, and accumulates dQ^T.
 // QI = 128: wave w takes queries 32w .. +31 against all 64 keys of a block.
 // QI = 64: wave w takes queries 32*(w%2) .. +31 against the block's keys
-// 32*(w/2) .. +31; the two waves of a query tile add their halves through LDS
-// at the end of the item (twice the items, for launches with few of them).
-// SUM: the D pass, which writes D_i = sum_j p_ij dp_ij to `delta`; otherwise
-// the dq pass, which reads it back and writes dq.
+// 32*(w/2) .. +31; the two waves of a query tile exchange their D sums and
+// add their dQ halves through LDS (twice the items, for launches with few
+// of them).
 //
 // Persistent workgroups, two per compute unit: a workgroup takes items
 // (numbered longest first: item j is query block qblocks-1-j/bh_count of
 // (b, h) = j % bh_count) in a snake over the grid (round r: item r*G + g for
 // even r, r*G + G-1-g for odd r), so heavy items pair with light ones.  While
-// an item's last key block is used, the next item's first block is already on
-// its way, and the next item's rows are loaded before this item's result is
-// stored.
-template <int D, bool SUM, int QI>
+// a pass's last key block is used, the next pass's (or the next item's)
+// first block is already on its way, and the next item's rows are loaded
+// before this item's result is stored.
+template <int D, int QI>
 __device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, const uint4* __restrict__ k,
                                                const uint4* __restrict__ v, const uint4* __restrict__ dout,
-                                               const float* __restrict__ lse, float* __restrict__ delta_io,
+                                               const float* __restrict__ lse, float* __restrict__ delta_out,
                                                uint2* __restrict__ dq, int seq, int heads, int qblocks, int bh_count,
                                                float scale2, float scale, const AttnSlopes& slopes) {
   static_assert(QI == 64 || QI == 128, "items of 64 or 128 queries");
@@ -231,7 +235,7 @@ __device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, cons
   if (j >= n_items) return;  // uniform over the workgroup
   // B operands: this lane's query row of q and dO (d = 16*kk + 8*half .. +8)
   bf16x8_t qf[KS], df[KS];
-  float lse2, delta = 0.f;
+  float lse2;
   auto load_rows = [&](int jn) {
     const int qb_ = qblocks - 1 - jn / bh_count;
     const int64_t bh_ = jn % bh_count;
@@ -248,10 +252,6 @@ __device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, cons
     }
     const float l = lse[row];
     lse2 = ok ? l * kLog2e : 0.f;
-    if (!SUM) {
-      const float d = delta_io[row];
-      delta = ok ? d : 0.f;
-    }
   };
   auto request_block = [&](int jn, int kb_, int stage) {
     const int64_t base_ = (int64_t)(jn % bh_count) * seq;
@@ -273,72 +273,83 @@ __device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, cons
     const bool wave_live = q0 < seq;
     const int jn = item_j(r + 1);
     const bool has_next = jn < n_items;
-
-    f32x16_t acc[DT];
-    if (!SUM) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
-    }
-    float dsum = 0.f;
     const int nkb = nkb_of(qb);  // key blocks nkb-1 .. 0
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    for (int kb = nkb - 1; kb >= 0; --kb, buf ^= 1) {
-      const int k0 = kb * kBwdRows;
-      const int kw0 = k0 + 32 * kh;  // this wave's first key of the block
-      // the next block arrives while this one is used (the barrier that
-      // ended the previous iteration freed its buffer)
-      if (kb >= 1)
-        request_block(j, kb - 1, buf ^ 1);
-      else if (has_next)
-        request_block(jn, nkb_of(qblocks - 1 - jn / bh_count) - 1, buf ^ 1);
-      if (wave_live && kw0 <= q0 + 31) {
-        if (kw0 + 32 * NKT - 1 > q0)
-          dq_block<D, true, SUM, NKT>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta, k0,
-                                      kh, qi, half, col, lane);
-        else
-          dq_block<D, false, SUM, NKT>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta,
-                                       k0, kh, qi, half, col, lane);
-      }
+    const bool writer = qvalid && kh == 0;
+
+    // One pass over the item's key blocks (SUM: the D pass); during its last
+    // block, block nkb_next-1 of item nj (if nvalid) is requested.
+    auto walk = [&](auto sum_tag, f32x16_t(&acc)[DT], float& dsum, float delta, int nj, int nkb_next, bool nvalid) {
+      constexpr bool SUM = decltype(sum_tag)::value;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-    }
+      for (int kb = nkb - 1; kb >= 0; --kb, buf ^= 1) {
+        const int k0 = kb * kBwdRows;
+        const int kw0 = k0 + 32 * kh;  // this wave's first key of the block
+        // the next block arrives while this one is used (the barrier that
+        // ended the previous iteration freed its buffer)
+        if (kb >= 1)
+          request_block(j, kb - 1, buf ^ 1);
+        else if (nvalid)
+          request_block(nj, nkb_next - 1, buf ^ 1);
+        if (wave_live && kw0 <= q0 + 31) {
+          if (kw0 + 32 * NKT - 1 > q0)
+            dq_block<D, true, SUM, NKT>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta,
+                                        k0, kh, qi, half, col, lane);
+          else
+            dq_block<D, false, SUM, NKT>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2,
+                                         delta, k0, kh, qi, half, col, lane);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      }
+    };
+
+    f32x16_t acc[DT];
+    // the D pass; then the same item's first block is on its way again
+    float dsum = 0.f;
+    walk(std::integral_constant<bool, true>(), acc, dsum, 0.f, j, nkb, true);
     // the two lane halves summed complementary keys of the same query
-    float dl = 0.f;
-    if (SUM) dl = dsum + __shfl_xor(dsum, 32, kWave);
+    float dl = dsum + __shfl_xor(dsum, 32, kWave);
     if (QI == 64) {
-      // the key-half-1 waves hand their sums to the key-half-0 waves of the
+      // both key-half waves of a query tile need the whole D: each hands its
+      // sum to the other through the stage the last block used (added in the
+      // same order on both sides)
+      float* xch = reinterpret_cast<float*>(&tiles[buf ^ 1][0][0]) + qt * (2 * kWave);
+      xch[kh * kWave + lane] = dl;
+      __syncthreads();
+      const float other = xch[(kh ^ 1) * kWave + lane];
+      dl = kh == 0 ? dl + other : other + dl;
+    }
+    if (writer && half == 0) delta_out[base + qi] = dl;
+
+    // the dq pass
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+    walk(std::integral_constant<bool, false>(), acc, dsum, qvalid ? dl : 0.f, jn,
+         has_next ? nkb_of(qblocks - 1 - jn / bh_count) : 1, has_next);
+    if (QI == 64) {
+      // the key-half-1 waves hand their dQ^T to the key-half-0 waves of the
       // same queries through the stage the last block used
       float* xch = reinterpret_cast<float*>(&tiles[buf ^ 1][0][0]) + qt * (DT * 16 * kWave);
       if (kh == 1) {
-        if (SUM) {
-          xch[lane] = dl;
-        } else {
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) xch[(dt * 16 + i) * kWave + lane] = acc[dt][i];
-        }
+          for (int i = 0; i < 16; ++i) xch[(dt * 16 + i) * kWave + lane] = acc[dt][i];
       }
       __syncthreads();
       if (kh == 0) {
-        if (SUM) {
-          dl += xch[lane];
-        } else {
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[dt][i] += xch[(dt * 16 + i) * kWave + lane];
-        }
+          for (int i = 0; i < 16; ++i) acc[dt][i] += xch[(dt * 16 + i) * kWave + lane];
       }
     }
-    const bool writer = qvalid && kh == 0;
-    if (SUM && writer && half == 0) delta_io[base + qi] = dl;
-    // this item's q, dO, lse and D are no longer needed: the next item's load now
+    // this item's q, dO and lse are no longer needed: the next item's load now
     if (has_next) load_rows(jn);
-    if (!SUM && writer) {
+    if (writer) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -354,23 +365,15 @@ __device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, cons
   }
 }
 
-// D pass: writes D_i for every query (FP32, [b*h*seq]).
+// D_i for every query (FP32, [b*h*seq], to `delta`) and
+// dq_i = scale * sum_j ds_ij k_j.
 template <int D, int QI>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_bwd_delta_kernel(
-    const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
-    const uint4* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ delta, int seq, int heads,
-    int qblocks, int bh_count, float scale2, AttnSlopes slopes) {
-  bwd_query_pass<D, true, QI>(q, k, v, dout, lse, delta, nullptr, seq, heads, qblocks, bh_count, scale2, 1.f, slopes);
-}
-
-// dq pass: dq_i = scale * sum_j ds_ij k_j with D_i from the D pass.
-template <int D, int QI>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_bwd_dq_kernel(
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_bwd_query_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
     const uint4* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ delta,
     uint2* __restrict__ dq, int seq, int heads, int qblocks, int bh_count, float scale2, float scale,
     AttnSlopes slopes) {
-  bwd_query_pass<D, false, QI>(q, k, v, dout, lse, delta, dq, seq, heads, qblocks, bh_count, scale2, scale, slopes);
+  bwd_query_pass<D, QI>(q, k, v, dout, lse, delta, dq, seq, heads, qblocks, bh_count, scale2, scale, slopes);
 }
 
 // ---------------------------------------------------------------------------
@@ -695,7 +698,7 @@ void launch_bwd(const bloom_bf16* q, const bloom_bf16* k, const bloom_bf16* v, c
                 const AttnSlopes& table, hipStream_t stream) {
   const int bh_count = (int)(batch * heads);
   const int blocks = (int)((seq + kBwdBlock - 1) / kBwdBlock);
-  // the D and dq kernels are persistent: two workgroups per compute unit, at
+  // the query-side kernel is persistent: two workgroups per compute unit, at
   // most one per item.  Items of 128 queries while they fill two rounds of
   // the grid, else of 64 (twice as many, so the causal work spreads evenly).
   const int64_t slots = 2 * (int64_t)(device_cu_count() > 0 ? device_cu_count() : 1);
@@ -707,19 +710,14 @@ void launch_bwd(const bloom_bf16* q, const bloom_bf16* k, const bloom_bf16* v, c
   const uint4* kv = reinterpret_cast<const uint4*>(k);
   const uint4* vv = reinterpret_cast<const uint4*>(v);
   const uint4* dov = reinterpret_cast<const uint4*>(dout);
-  if (wide) {
-    hipLaunchKernelGGL((attention_bwd_delta_kernel<D, 128>), grid_q, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov,
-                       lse, delta, (int)seq, (int)heads, qblocks, bh_count, scale2, table);
-    hipLaunchKernelGGL((attention_bwd_dq_kernel<D, 128>), grid_q, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov, lse,
-                       delta, reinterpret_cast<uint2*>(dq), (int)seq, (int)heads, qblocks, bh_count, scale2, scale,
-                       table);
-  } else {
-    hipLaunchKernelGGL((attention_bwd_delta_kernel<D, 64>), grid_q, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov,
-                       lse, delta, (int)seq, (int)heads, qblocks, bh_count, scale2, table);
-    hipLaunchKernelGGL((attention_bwd_dq_kernel<D, 64>), grid_q, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov, lse,
-                       delta, reinterpret_cast<uint2*>(dq), (int)seq, (int)heads, qblocks, bh_count, scale2, scale,
-                       table);
-  }
+  if (wide)
+    hipLaunchKernelGGL((attention_bwd_query_kernel<D, 128>), grid_q, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov,
+                       lse, delta, reinterpret_cast<uint2*>(dq), (int)seq, (int)heads, qblocks, bh_count, scale2,
+                       scale, table);
+  else
+    hipLaunchKernelGGL((attention_bwd_query_kernel<D, 64>), grid_q, dim3(kBwdThreads), 0, stream, qv, kv, vv, dov,
+                       lse, delta, reinterpret_cast<uint2*>(dq), (int)seq, (int)heads, qblocks, bh_count, scale2,
+                       scale, table);
   // the dk/dv kernel is persistent too: one eight-wave workgroup per compute unit
   const int64_t kv_items = (int64_t)bh_count * blocks;
   const int64_t cus = slots / 2;

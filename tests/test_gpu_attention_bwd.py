@@ -108,7 +108,7 @@ def test_attention_fwd_then_bwd_long_context_sampled():
 
 
 def _wide_items(b, h, s):
-    """Whether the backward's D and dq kernels take items of 128 queries on
+    """Whether the backward's query-side kernel takes items of 128 queries on
     this GPU (else 64): when the 128-query items fill two rounds of two
     workgroups per compute unit."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
