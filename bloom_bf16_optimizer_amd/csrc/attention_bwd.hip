@@ -499,6 +499,39 @@ __device__ __forceinline__ void dk_tile(f32x16_t (&dkacc)[D / 32], const f32x16_
     }
 }
 
+// An item of the dk/dv kernel (128 keys of one (b, h)), numbered heaviest
+// first: hb is its key block (block 0 meets every query, so it is the
+// heaviest), bh its (b, h).  With xs, item j belongs to XCD j % 8: every
+// (b, h) is cut into its key blocks of either parity and XCD x takes
+// half-heads [x*n, (x+1)*n), so an XCD's L2 holds the Q and dO of at most
+// n/2 + 1 heads.  Otherwise items walk the key blocks from the first, every
+// (b, h) at each step.
+struct BwdItem {
+  int hb;
+  int64_t bh;
+};
+__device__ __forceinline__ BwdItem bwd_item(int j, int nblocks, int bh_count, bool xs) {
+  BwdItem it;
+  if (xs) {
+    const int x = j % 8, jj = j / 8;
+    const int n = bh_count / 4;  // half-heads per XCD
+    const int rank = jj / n, hh = n * x + jj % n, par = hh & 1;
+    it.bh = hh >> 1;
+    it.hb = ((nblocks - 1 - par) & 1) + 2 * rank;
+  } else {
+    it.hb = j / bh_count;
+    it.bh = j % bh_count;
+  }
+  return it;
+}
+// Item of round r for workgroup g of G: a snake over the grid, or with xs
+// over the G/8 workgroups of g's XCD (workgroup g runs on XCD g % 8).
+__device__ __forceinline__ int bwd_round_item(int r, int g, int G, bool xs) {
+  if (!xs) return r * G + ((r & 1) ? G - 1 - g : g);
+  const int U = G / 8, u = g / 8;
+  return (r * U + ((r & 1) ? U - 1 - u : u)) * 8 + g % 8;
+}
+
 constexpr int kKvWaves = 8;
 constexpr int kKvThreads = kKvWaves * kWave;
 
@@ -514,16 +547,15 @@ struct KvShared {
 // role is a template parameter and each role's registers are allocated alone.
 //
 // Persistent workgroups, one per compute unit: a workgroup takes items (128
-// keys of one (b, h), numbered longest first: item j is key block j/bh_count
-// of (b, h) = j % bh_count) in a snake over the grid, as the query-side
-// kernels do.  The next block (or the next item's first block) is in flight
-// while a block is used.
+// keys of one (b, h), numbered longest first, see bwd_item) in a snake over
+// its XCD's workgroups (xs) or over the grid.  The next block (or the next
+// item's first block) is in flight while a block is used.
 template <int D, bool DSW>
 __device__ __forceinline__ void dkdv_walk(KvShared<D>& sh, const uint4* __restrict__ q, const uint4* __restrict__ k,
                                           const uint4* __restrict__ v, const uint4* __restrict__ dout,
                                           const float* __restrict__ lse, const float* __restrict__ delta,
                                           uint2* __restrict__ out, int seq, int heads, int kblocks, int bh_count,
-                                          float scale2, float outscale, const AttnSlopes& slopes) {
+                                          bool xs, float scale2, float outscale, const AttnSlopes& slopes) {
   constexpr int KS = D / 16, DT = D / 32, VPR = D / 8;
   constexpr int CH = BwdTile<D>::CHUNKS;
   const int t = threadIdx.x;
@@ -534,7 +566,9 @@ __device__ __forceinline__ void dkdv_walk(KvShared<D>& sh, const uint4* __restri
 
   const int G = (int)gridDim.x, g = (int)blockIdx.x;
   const int n_items = kblocks * bh_count;
-  auto item_j = [&](int r) { return r * G + ((r & 1) ? G - 1 - g : g); };
+  auto item_j = [&](int r) { return bwd_round_item(r, g, G, xs); };
+  auto kb_of = [&](int jn) { return bwd_item(jn, kblocks, bh_count, xs).hb; };
+  auto bh_of = [&](int jn) { return bwd_item(jn, kblocks, bh_count, xs).bh; };
   const int nqb = (seq + kBwdRows - 1) / kBwdRows;
 
   int j = item_j(0);
@@ -544,9 +578,9 @@ __device__ __forceinline__ void dkdv_walk(KvShared<D>& sh, const uint4* __restri
   // d = 16*kk + 8*half .. +8; keys past seq read row seq-1 and are zeroed
   bf16x8_t kv[KS];
   auto load_keys = [&](int jn) {
-    const int kj_ = (jn / bh_count) * kBwdBlock + kgrp * 32 + col;
+    const int kj_ = kb_of(jn) * kBwdBlock + kgrp * 32 + col;
     const bool ok = kj_ < seq;
-    const int64_t row = (int64_t)(jn % bh_count) * seq + min(kj_, seq - 1);
+    const int64_t row = bh_of(jn) * seq + min(kj_, seq - 1);
     const uint4* src = DSW ? v : k;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -570,18 +604,18 @@ __device__ __forceinline__ void dkdv_walk(KvShared<D>& sh, const uint4* __restri
     bwd_request<D, kKvWaves>(q, tile(stage, 0), base_, qb_ * kBwdRows, seq, w, lane);
     bwd_request<D, kKvWaves>(dout, tile(stage, 1), base_, qb_ * kBwdRows, seq, w, lane);
   };
-  auto first_qb = [&](int jn) { return ((jn / bh_count) * kBwdBlock) / kBwdRows; };  // block of the item's first key
+  auto first_qb = [&](int jn) { return (kb_of(jn) * kBwdBlock) / kBwdRows; };  // block of the item's first key
 
   load_keys(j);
   {
-    const int64_t base0 = (int64_t)(j % bh_count) * seq;
+    const int64_t base0 = bh_of(j) * seq;
     request_block(base0, first_qb(j), 0);
     if (!DSW && t < 32) row_store(0, row_load(base0, first_qb(j) * kBwdRows));
   }
   int buf = 0;  // the stage holding the next block to use
   for (int r = 0;; ++r) {
-    const int kb = j / bh_count;
-    const int64_t bh = j % bh_count;
+    const int kb = kb_of(j);
+    const int64_t bh = bh_of(j);
     const int h = (int)(bh % heads);
     const float slope2 = slopes.s[h];
     const int64_t base = bh * (int64_t)seq;
@@ -610,7 +644,7 @@ __device__ __forceinline__ void dkdv_walk(KvShared<D>& sh, const uint4* __restri
         request_block(base, qbi + 1, buf ^ 1);
         if (!DSW && t < 32) rv = row_load(base, q0 + kBwdRows);
       } else if (has_next) {
-        const int64_t bn = (int64_t)(jn % bh_count) * seq;
+        const int64_t bn = bh_of(jn) * seq;
         request_block(bn, first_qb(jn), buf ^ 1);
         if (!DSW && t < 32) rv = row_load(bn, first_qb(jn) * kBwdRows);
       }
@@ -679,13 +713,13 @@ template <int D>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_bwd_dkdv_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
     const uint4* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    uint2* __restrict__ dk, uint2* __restrict__ dv, int seq, int heads, int kblocks, int bh_count, float scale2,
-    float scale, AttnSlopes slopes) {
+    uint2* __restrict__ dk, uint2* __restrict__ dv, int seq, int heads, int kblocks, int bh_count, bool xs,
+    float scale2, float scale, AttnSlopes slopes) {
   __shared__ __attribute__((aligned(16))) KvShared<D> sh;
   if (threadIdx.x >= 4 * kWave)  // wave-uniform: waves 4..7 are the dS waves
-    dkdv_walk<D, true>(sh, q, k, v, dout, lse, delta, dk, seq, heads, kblocks, bh_count, scale2, scale, slopes);
+    dkdv_walk<D, true>(sh, q, k, v, dout, lse, delta, dk, seq, heads, kblocks, bh_count, xs, scale2, scale, slopes);
   else
-    dkdv_walk<D, false>(sh, q, k, v, dout, lse, delta, dv, seq, heads, kblocks, bh_count, scale2, 1.f, slopes);
+    dkdv_walk<D, false>(sh, q, k, v, dout, lse, delta, dv, seq, heads, kblocks, bh_count, xs, scale2, 1.f, slopes);
 }
 
 size_t bwd_workspace(int64_t batch, int32_t heads, int64_t seq) {
@@ -721,10 +755,14 @@ void launch_bwd(const bloom_bf16* q, const bloom_bf16* k, const bloom_bf16* v, c
   // the dk/dv kernel is persistent too: one eight-wave workgroup per compute unit
   const int64_t kv_items = (int64_t)bh_count * blocks;
   const int64_t cus = slots / 2;
+  // whole half-heads per XCD (an even number of key blocks, (b, h) pairs a
+  // multiple of 4, a grid of whole XCD rounds): each XCD's L2 holds the Q
+  // and dO of about a quarter of the heads it would otherwise stream
+  const bool xs_kv = blocks % 2 == 0 && bh_count % 4 == 0 && cus % 8 == 0;
   const dim3 grid_kv((unsigned)(kv_items < cus ? kv_items : cus));
   hipLaunchKernelGGL((attention_bwd_dkdv_kernel<D>), grid_kv, dim3(kKvThreads), 0, stream, qv, kv, vv, dov, lse,
                      delta, reinterpret_cast<uint2*>(dk), reinterpret_cast<uint2*>(dv), (int)seq, (int)heads, blocks,
-                     bh_count, scale2, scale, table);
+                     bh_count, xs_kv, scale2, scale, table);
 }
 
 }  // namespace
