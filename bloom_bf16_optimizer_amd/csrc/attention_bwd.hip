@@ -115,13 +115,20 @@ __device__ __forceinline__ bf16x8_t bwd_read_tr(const char __attribute__((addres
   return as_bf16x8(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
 }
 
-// x as hi + lo, both bf16: hi = RNE(x), lo = RNE(x - hi) (x - hi is exact in FP32).
-struct Bf16Pair {
-  __bf16 hi, lo;
+// Two products a0*b0, a1*b1 as hi + lo pairs of bf16, packed two to a
+// dword (element 0 in the low half): hi = RNE(a*b), lo = RNE(a*b - hi) with
+// the residual formed by one fma from the exact product.
+struct Bf16Split2 {
+  uint32_t hi, lo;
 };
-__device__ __forceinline__ Bf16Pair split_bf16(float x) {
-  const __bf16 hi = (__bf16)x;
-  return {hi, (__bf16)(x - (float)hi)};
+__device__ __forceinline__ Bf16Split2 split_bf16x2(float a0, float b0, float a1, float b1) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t x = {a0 * b0, a1 * b1};
+  const uint32_t hu = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+  const float h0 = __uint_as_float(hu << 16), h1 = __uint_as_float(hu & 0xffff0000u);
+  const f32x2_t r = {fmaf(a0, b0, -h0), fmaf(a1, b1, -h1)};
+  return {hu, __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t))};
 }
 
 // ---------------------------------------------------------------------------
@@ -161,7 +168,8 @@ __device__ __forceinline__ void dq_block(f32x16_t (&acc)[D / 32], float& dsum, c
       s = mfma32(__builtin_bit_cast(bf16x8_t, k0r[c]), qf[kk], s);
       dp = mfma32(__builtin_bit_cast(bf16x8_t, v0r[c]), df[kk], dp);
     }
-    bf16x8_t dsh[2], dsl[2];
+    attn_u32x4 dsh[2], dsl[2];  // the bf16x8 operands of each part, as dwords
+    float pp[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int off = 32 * kt + 8 * (i / 4) + (i % 4);  // key - k0 - 4*half
@@ -170,9 +178,12 @@ __device__ __forceinline__ void dq_block(f32x16_t (&acc)[D / 32], float& dsum, c
       if (SUM) {
         dsum = fmaf(p, dp[i], dsum);
       } else {
-        const Bf16Pair d2 = split_bf16(p * (dp[i] - delta));
-        dsh[i / 8][i % 8] = d2.hi;
-        dsl[i / 8][i % 8] = d2.lo;
+        pp[i & 1] = p;
+        if (i & 1) {
+          const Bf16Split2 d2 = split_bf16x2(pp[0], dp[i - 1] - delta, pp[1], dp[i] - delta);
+          dsh[i / 8][(i % 8) / 2] = d2.hi;
+          dsl[i / 8][(i % 8) / 2] = d2.lo;
+        }
       }
     }
     if (!SUM) {
@@ -181,8 +192,8 @@ __device__ __forceinline__ void dq_block(f32x16_t (&acc)[D / 32], float& dsum, c
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const bf16x8_t kT = bwd_read_tr<D>(kbytes, 16 * (2 * kt + st2), dt, trow, tg, tc, sw0, sw8);
-          acc[dt] = mfma32(kT, dsh[st2], acc[dt]);
-          acc[dt] = mfma32(kT, dsl[st2], acc[dt]);
+          acc[dt] = mfma32(kT, __builtin_bit_cast(bf16x8_t, dsh[st2]), acc[dt]);
+          acc[dt] = mfma32(kT, __builtin_bit_cast(bf16x8_t, dsl[st2]), acc[dt]);
         }
     }
   }
@@ -470,18 +481,18 @@ __device__ __forceinline__ void dk_tile(f32x16_t (&dkacc)[D / 32], const f32x16_
                                         int half, int lane) {
   using T = BwdTile<D>;
   constexpr int DT = D / 32;
-  bf16x8_t dsh[2], dsl[2];
+  attn_u32x4 dsh[2], dsl[2];  // the bf16x8 operands of each part, as dwords
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const float4 p4 = pin[g * kWave + lane];
     const float4 d4 = delta_lds[(tr0 + 8 * g + 4 * half) / 4];
     const float pv[4] = {p4.x, p4.y, p4.z, p4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < 4; r += 2) {
       const int i = 4 * g + r;
-      const Bf16Pair d2 = split_bf16(pv[r] * (dp[i] - dv4[r]));
-      dsh[i / 8][i % 8] = d2.hi;
-      dsl[i / 8][i % 8] = d2.lo;
+      const Bf16Split2 d2 = split_bf16x2(pv[r], dp[i] - dv4[r], pv[r + 1], dp[i + 1] - dv4[r + 1]);
+      dsh[i / 8][(i % 8) / 2] = d2.hi;
+      dsl[i / 8][(i % 8) / 2] = d2.lo;
     }
   }
   const int tj = (lane & 15) >> 2, tc = lane & 3, tg = (lane >> 4) & 1;
@@ -494,8 +505,8 @@ __device__ __forceinline__ void dk_tile(f32x16_t (&dkacc)[D / 32], const f32x16_
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const bf16x8_t qT = bwd_read_tr<D>(qbytes, tr0 + 16 * stp, dt, trow, tg, tc, sw0, sw8);
-      dkacc[dt] = mfma32(qT, dsh[stp], dkacc[dt]);
-      dkacc[dt] = mfma32(qT, dsl[stp], dkacc[dt]);
+      dkacc[dt] = mfma32(qT, __builtin_bit_cast(bf16x8_t, dsh[stp]), dkacc[dt]);
+      dkacc[dt] = mfma32(qT, __builtin_bit_cast(bf16x8_t, dsl[stp]), dkacc[dt]);
     }
 }
 
