@@ -88,6 +88,18 @@ __device__ __forceinline__ void bwd_request(const uint4* __restrict__ g, attn_ld
   if (w >= DW) return;  // wave-uniform
   const uint4* gb = attn_uniform(g + (base + r0) * T::CPR);
   const bool tail = r0 + kBwdRows > seq;  // wave-uniform
+  if (!tail) {
+    // Transfer x moves chunks DW*64*x further on in both the tile and the
+    // rows: DW*64/CPR rows, a multiple of swz's period of 16 rows, so every
+    // transfer has the first one's lane offset and a uniform step of DW KB.
+    const int slot = w * kWave + lane;
+    const int r = slot / T::CPR, c = (slot % T::CPR) ^ T::swz(r);
+    const uint32_t vo = (uint32_t)(r * T::CPR + c) * 16u;
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(tile + w * kWave));
+#pragma unroll
+    for (int x = 0; x < PER; ++x) attn_dma16(gb + x * DW * kWave, vo, m0 + (uint32_t)(x * DW * kWave * 16));
+    return;
+  }
 #pragma unroll
   for (int x = 0; x < PER; ++x) {
     const int first = (DW * x + w) * kWave;
@@ -95,7 +107,7 @@ __device__ __forceinline__ void bwd_request(const uint4* __restrict__ g, attn_ld
     const int r = slot / T::CPR, pc = slot % T::CPR;
     const int c = pc ^ T::swz(r);
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(tile + first));
-    const int row = tail ? min(r, seq - 1 - r0) : r;
+    const int row = min(r, seq - 1 - r0);
     attn_dma16(gb, (uint32_t)(row * T::CPR + c) * 16u, m0);
   }
 }
