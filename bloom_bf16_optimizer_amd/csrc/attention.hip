@@ -64,8 +64,8 @@ struct AttnTile {
 
 // Requests key block [k0, k0+64) of K (SWZ_V false) or V into `tile`; this
 // wave (wq of the stream's four) moves chunks [64*(4x + wq), +64) for each
-// x.  A lane's chunk offset within the block does not depend on k0 (so it
-// stays in a register across blocks); only the block at the end of the
+// x.  A lane's chunk offset within the block does not depend on k0 or x (so
+// it stays in a register across blocks); only the block at the end of the
 // sequence re-reads row seq-1 for its rows past the end (their keys are
 // masked for every query that is stored).
 template <int D, bool SWZ_V>
@@ -76,6 +76,20 @@ __device__ __forceinline__ void attn_request(const uint4* __restrict__ g, attn_l
   const uint4* gb = (const uint4*)(uintptr_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(gp >> 32)) << 32) |
                                                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)gp));
   const bool tail = k0 + kAttnBlockN > seq;  // wave-uniform
+  if (!tail) {
+    // Transfer x moves 256 chunks further on in both the block and its
+    // rows: 256/CPR rows, a multiple of both swizzles' periods (16 and 4
+    // rows), so every transfer has the first one's lane offset and a
+    // uniform step of 4 KB in the scalar base and in m0.
+    const int slot = wq * kWave + lane;
+    const int r = slot / T::CPR, c = (slot % T::CPR) ^ (SWZ_V ? T::swz_v(r) : T::swz_k(r));
+    const uint32_t vo = (uint32_t)(r * T::CPR + c) * 16u;
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(tile + wq * kWave));
+#pragma unroll
+    for (int x = 0; x < T::DMA; ++x)
+      attn_dma16(gb + x * kAttnGroupThreads, vo, m0 + (uint32_t)(x * kAttnGroupThreads * 16));
+    return;
+  }
 #pragma unroll
   for (int x = 0; x < T::DMA; ++x) {
     const int first = (4 * x + wq) * kWave;
@@ -83,7 +97,7 @@ __device__ __forceinline__ void attn_request(const uint4* __restrict__ g, attn_l
     const int r = slot / T::CPR, pc = slot % T::CPR;
     const int c = pc ^ (SWZ_V ? T::swz_v(r) : T::swz_k(r));
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(tile + first));
-    const int row = tail ? min(r, seq - 1 - k0) : r;
+    const int row = min(r, seq - 1 - k0);
     attn_dma16(gb, (uint32_t)(row * T::CPR + c) * 16u, m0);
   }
 }
