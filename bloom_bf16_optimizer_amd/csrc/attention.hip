@@ -404,7 +404,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     const int nkb = nkb_of(qb);
     const int iters = (nkb + 1) / 2;
     int kb = nkb - 1 - stream;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    attn_wait_loads();
     __syncthreads();
     for (int it = 0, buf = 0; it < iters; ++it, buf ^= 1, kb -= 2) {
       const int k0 = kb * kAttnBlockN;
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
         else
           attn_block<D, false>(st, tile(buf, 0), tile(buf, 1), qf, kx, qx, scale2, slope2, k0, qi, half, col, lane);
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      attn_wait_loads();
       __syncthreads();
     }
 
@@ -509,7 +509,7 @@ __global__ __launch_bounds__(kAttnGroupThreads) __attribute__((amdgpu_waves_per_
   int kb = nkb - 1;
   attn_request<D, false>(k, tile(0, 0), base, kb * kAttnBlockN, seq, w, lane);
   attn_request<D, true>(v, tile(0, 1), base, kb * kAttnBlockN, seq, w, lane);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  attn_wait_loads();
   __syncthreads();
   for (int buf = 0; kb >= 0; buf ^= 1, --kb) {
     const int k0 = kb * kAttnBlockN;
@@ -524,7 +524,7 @@ __global__ __launch_bounds__(kAttnGroupThreads) __attribute__((amdgpu_waves_per_
         attn_block<D, false, true>(st, tile(buf, 0), tile(buf, 1), qf, kx, qx, scale2, slope2, k0, qi, half, col,
                                    lane);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    attn_wait_loads();
     __syncthreads();
   }
   attn_store_row<D>(st, o, lse, base + qi, qi < seq, half);

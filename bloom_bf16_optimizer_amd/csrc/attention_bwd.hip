@@ -303,7 +303,7 @@ __device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, cons
     // block, block nkb_next-1 of item nj (if nvalid) is requested.
     auto walk = [&](auto sum_tag, f32x16_t(&acc)[DT], float& dsum, float delta, int nj, int nkb_next, bool nvalid) {
       constexpr bool SUM = decltype(sum_tag)::value;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      attn_wait_loads();
       __syncthreads();
       for (int kb = nkb - 1; kb >= 0; --kb, buf ^= 1) {
         const int k0 = kb * kBwdRows;
@@ -322,7 +322,7 @@ __device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, cons
             dq_block<D, false, SUM, NKT>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2,
                                          delta, k0, kh, qi, half, col, lane);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        attn_wait_loads();
         __syncthreads();
       }
     };
@@ -655,22 +655,23 @@ __device__ __forceinline__ void dkdv_walk(KvShared<D>& sh, const uint4* __restri
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    attn_wait_loads();
     __syncthreads();
     for (int qbi = first_qb(j); qbi < nqb; ++qbi, buf ^= 1) {
       const int q0 = qbi * kBwdRows;
       const bool next = qbi + 1 < nqb;
-      float4 rv = make_float4(0.f, 0.f, 0.f, 0.f);
-      // the next block arrives while this one is used (the barrier that
-      // ended the previous iteration freed its buffer)
-      if (next) {
-        request_block(base, qbi + 1, buf ^ 1);
-        if (!DSW && t < 32) rv = row_load(base, q0 + kBwdRows);
-      } else if (has_next) {
-        const int64_t bn = bh_of(jn) * seq;
-        request_block(bn, first_qb(jn), buf ^ 1);
-        if (!DSW && t < 32) rv = row_load(bn, first_qb(jn) * kBwdRows);
-      }
+      // the next block (this item's, or the next item's first) arrives while
+      // this one is used (the barrier that ended the previous iteration freed
+      // its buffer)
+      const bool rnext = next || has_next;
+      const int64_t nbase = next || !has_next ? base : bh_of(jn) * seq;
+      const int nqb0 = next ? qbi + 1 : (has_next ? first_qb(jn) : qbi);
+      if (rnext) request_block(nbase, nqb0, buf ^ 1);
+      // its row values (P waves, t < 32): one load, used only by the store at
+      // the end of the block, so the compiler waits for it there and not
+      // earlier (any earlier wait would also drain the transfers just issued)
+      float4 rv;
+      if (!DSW && t < 32) rv = row_load(nbase, nqb0 * kBwdRows);
       bool live[2], mask[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -709,9 +710,9 @@ __device__ __forceinline__ void dkdv_walk(KvShared<D>& sh, const uint4* __restri
           __syncthreads();  // P of tile tt is in LDS for the dS waves
         }
         if (live[1]) dv_tile<D>(acc, pf[1], tile(buf, 1), 32, half, lane);
-        if ((next || has_next) && t < 32) row_store(buf ^ 1, rv);
+        if (rnext && t < 32) row_store(buf ^ 1, rv);
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      attn_wait_loads();
       __syncthreads();
     }
     // this item's key rows are no longer needed: the next item's load now

@@ -42,6 +42,19 @@ __device__ __forceinline__ void attn_dma16(const void* sbase, uint32_t voff, uin
                : "memory", "m0");
 }
 
+// Waits for every vector-memory load of the wave, the direct-to-LDS tile
+// transfers included (they are inline asm, which the compiler does not
+// track), and tells the compiler so.  Without the second, compiler-visible
+// wait it takes its own loads issued before a block loop (the next item's
+// rows) as still pending and waits for them again at their first use inside
+// the loop, on every block; that wait, counted in hardware, also drains the
+// next block's transfers issued just before, so the block would wait for its
+// successor's tiles.
+__device__ __forceinline__ void attn_wait_loads() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt not waited for
+}
+
 // A 64-bit pointer made wave-uniform (both halves through readfirstlane), so
 // that it can sit in the SGPR pair the transfer instruction takes.
 template <typename T>
