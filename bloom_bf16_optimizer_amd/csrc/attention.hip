@@ -134,6 +134,9 @@ __device__ __forceinline__ void attn_block(AttnState<D>& st, const attn_lds_uint
   // reads chunk 2*kk + half of K rows col and 32 + col (same swizzle).
   const f32x16_t zero = {};
   f32x16_t s[2];
+  // the score products at a raised issue priority: the other wave of the
+  // SIMD then fills the gaps of this chain instead of delaying it
+  __builtin_amdgcn_s_setprio(1);
   s[0] = mfma32(kx[0], qx, zero);
   s[1] = mfma32(kx[1], qx, zero);
   const int sk = T::swz_k(col);
@@ -146,6 +149,7 @@ __device__ __forceinline__ void attn_block(AttnState<D>& st, const attn_lds_uint
     s[0] = mfma32(__builtin_bit_cast(bf16x8_t, a0), qf[kk], s[0]);
     s[1] = mfma32(__builtin_bit_cast(bf16x8_t, a1), qf[kk], s[1]);
   }
+  __builtin_amdgcn_s_setprio(0);
   if (DIAG) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)

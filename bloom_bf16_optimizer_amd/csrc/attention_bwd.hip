@@ -174,12 +174,16 @@ __device__ __forceinline__ void dq_block(f32x16_t (&acc)[D / 32], float& dsum, c
   for (int u = 0; u < NKT; ++u) {
     const int kt = kt0 + u;
     f32x16_t s = zero, dp = zero;
+    // the score products at a raised issue priority: the other wave of the
+    // SIMD then fills the gaps of this chain instead of delaying it
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const int c = 32 * kt * T::CPR + ((2 * kk + half) ^ sw);
       s = mfma32(__builtin_bit_cast(bf16x8_t, k0r[c]), qf[kk], s);
       dp = mfma32(__builtin_bit_cast(bf16x8_t, v0r[c]), df[kk], dp);
     }
+    __builtin_amdgcn_s_setprio(0);
     attn_u32x4 dsh[2], dsl[2];  // the bf16x8 operands of each part, as dwords
     float pp[2];
 #pragma unroll
@@ -428,8 +432,10 @@ __device__ __forceinline__ void p_tile(bf16x8_t (&pf)[2], float4* __restrict__ p
   f32x16_t s = {};
   const int sw = T::swz(tr0 + col);
   const attn_lds_u32x4* qr = reinterpret_cast<const attn_lds_u32x4*>(q_lds) + (tr0 + col) * T::CPR;
+  __builtin_amdgcn_s_setprio(1);  // as in dq_block
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) s = mfma32(__builtin_bit_cast(bf16x8_t, qr[(2 * kk + half) ^ sw]), kf[kk], s);
+  __builtin_amdgcn_s_setprio(0);
   // base-2 logit minus lse: s*scale2 + slope2*(kj - query) - lse2(query)
   const float cb = slope2 * (float)(kj - qt0 - 4 * half);
 #pragma unroll
@@ -480,8 +486,10 @@ __device__ __forceinline__ f32x16_t dp_tile(const attn_lds_uint4* __restrict__ d
   f32x16_t dp = {};
   const int sw = T::swz(tr0 + col);
   const attn_lds_u32x4* dr = reinterpret_cast<const attn_lds_u32x4*>(do_lds) + (tr0 + col) * T::CPR;
+  __builtin_amdgcn_s_setprio(1);  // as in dq_block
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) dp = mfma32(__builtin_bit_cast(bf16x8_t, dr[(2 * kk + half) ^ sw]), vf[kk], dp);
+  __builtin_amdgcn_s_setprio(0);
   return dp;
 }
 
