@@ -319,24 +319,47 @@ __device__ __forceinline__ void attn_state_init(AttnState<D>& st) {
   st.l = 0.f;
 }
 
-// Normalise and store a finished row: the two lane halves hold the sums over
-// complementary keys; lane half h holds d = 32*dt + 8*g + 4*h + 0..3.
+// A finished row, normalised, into a staged output tile: the two lane halves
+// hold the sums over complementary keys; lane half h holds
+// d = 32*dt + 8*g + 4*h + 0..3 of row `row` (0..127) of the tile, bf16
+// row-major with 16-byte chunk c of row r at c ^ (r % CPR), so that the
+// writes of 32 rows and the whole-row reads of attn_store_tile are free of
+// bank conflicts.  Also writes the row's lse (natural log) if ok.
 template <int D>
-__device__ __forceinline__ void attn_store_row(const AttnState<D>& st, uint2* __restrict__ o, float* __restrict__ lse,
-                                               int64_t row, bool ok, int half) {
+__device__ __forceinline__ void attn_row_to_tile(const AttnState<D>& st, char* otile, int row, float* __restrict__ lse,
+                                                 int64_t lrow, bool ok, int half) {
+  constexpr int CPR = D / 8;
   const float l_tot = st.l + __shfl_xor(st.l, 32, kWave);
   const float inv = 1.0f / l_tot;
-  if (!ok) return;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint32_t lo = pack2(st.oacc[dt][4 * g] * inv, st.oacc[dt][4 * g + 1] * inv);
       const uint32_t hi = pack2(st.oacc[dt][4 * g + 2] * inv, st.oacc[dt][4 * g + 3] * inv);
-      o[row * (D / 4) + (32 * dt + 8 * g + 4 * half) / 4] = make_uint2(lo, hi);
+      const int c = (4 * dt + g) ^ (row % CPR);
+      *reinterpret_cast<uint2*>(otile + row * (2 * D) + 16 * c + 8 * half) = make_uint2(lo, hi);
     }
+  if (ok && half == 0) lse[lrow] = (st.m + __log2f(l_tot)) * 0.69314718055994530942f;
+}
+
+// The staged output tile of 128 rows to o rows row0 .. (rows past `valid`
+// are not stored): NT threads store whole rows, 16 bytes each, instead of
+// each lane storing 8-byte pieces of 16 different rows.
+template <int D, int NT>
+__device__ __forceinline__ void attn_store_tile(const char* otile, uint2* __restrict__ o, int64_t row0, int valid,
+                                                int t) {
+  constexpr int CPR = D / 8;
+  constexpr int PER = kAttnBlockM * CPR / NT;  // 16-byte chunks per thread
+  static_assert(PER >= 1 && kAttnBlockM * CPR % NT == 0, "output tile chunks");
+  uint4* o4 = reinterpret_cast<uint4*>(o);
+#pragma unroll
+  for (int x = 0; x < PER; ++x) {
+    const int chunk = x * NT + t;
+    const int row = chunk / CPR, c = chunk % CPR;
+    const uint4 val = *reinterpret_cast<const uint4*>(otile + row * (2 * D) + 16 * (c ^ (row % CPR)));
+    if (row < valid) o4[(row0 + row) * CPR + c] = val;
   }
-  if (half == 0) lse[row] = (st.m + __log2f(l_tot)) * 0.69314718055994530942f;
 }
 
 template <int D>
@@ -430,11 +453,9 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
       __syncthreads();
     }
 
-    // The next item's Q arrives during the merge (this item's Q is done).
     const int jn = item_index(r + 1);
     const bool has_next = jn < n_items;
     const AttnItem nxt = attn_item(has_next ? jn : j, qblocks, bh_count, xcd_split);
-    if (has_next) attn_load_q<D>(qf, q, nxt.bh * (int64_t)seq + q_row(nxt), q_row(nxt) < seq, half);
 
     // Merge stream 1 into stream 0 through LDS ([wave][value][lane] floats).
     // Block 0 is processed by one of the streams for every live row, so at
@@ -449,6 +470,8 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
       mg[(DT * 16 + 1) * kWave] = st.l;
     }
     __syncthreads();
+    // the next item's Q arrives during the merge (this item's Q is done)
+    if (has_next) attn_load_q<D>(qf, q, nxt.bh * (int64_t)seq + q_row(nxt), q_row(nxt) < seq, half);
     if (stream == 0) {
       const float m1 = mg[(DT * 16) * kWave], l1 = mg[(DT * 16 + 1) * kWave];
       const float m = fmaxf(st.m, m1);
@@ -460,11 +483,19 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
       st.l = fmaf(st.l, a0, l1 * a1);
       st.m = m;
     }
+    // Stream 0 puts the normalised rows in LDS (the last 256*D bytes of the
+    // tiles, past the merge area), and all eight waves store them.
+    char* otile = reinterpret_cast<char*>(&tiles[0][0][0][0]) + sizeof(tiles) - kAttnBlockM * D * 2;
+    static_assert(sizeof(tiles) - kAttnBlockM * D * 2 >= 4 * (DT * 16 + 2) * kWave * sizeof(float),
+                  "output tile past the merge area");
+    if (stream == 0) attn_row_to_tile<D>(st, otile, wq * 32 + col, lse, base + qi, qi < seq, half);
     // The merge area is the next item's tile memory: every read of it ends
-    // here, and the next item's first key blocks are requested right after.
+    // here, and the next item's first key blocks are requested right after
+    // (the output tile lies in the other stage, which the next item first
+    // refills after its own first barrier).
     __syncthreads();
     if (has_next) request_first(nxt);
-    if (stream == 0) attn_store_row<D>(st, o, lse, base + qi, qi < seq, half);
+    attn_store_tile<D, kAttnThreads>(otile, o, base + qb * kAttnBlockM, seq - qb * kAttnBlockM, t);
     if (!has_next) break;  // uniform over the workgroup
     j = jn;
     cur = nxt;
@@ -531,7 +562,12 @@ __global__ __launch_bounds__(kAttnGroupThreads) __attribute__((amdgpu_waves_per_
     attn_wait_loads();
     __syncthreads();
   }
-  attn_store_row<D>(st, o, lse, base + qi, qi < seq, half);
+  // the tiles are free after the last barrier: the rows go through them
+  char* otile = reinterpret_cast<char*>(&tiles[0][0][0]);
+  static_assert(sizeof(tiles) >= kAttnBlockM * D * 2, "output tile");
+  attn_row_to_tile<D>(st, otile, w * 32 + col, lse, base + qi, qi < seq, half);
+  __syncthreads();
+  attn_store_tile<D, kAttnGroupThreads>(otile, o, base + qb * kAttnBlockM, seq - qb * kAttnBlockM, t);
 }
 
 bloom_status check_attention(int64_t batch, int32_t heads, int64_t seq, int32_t head_dim) {
