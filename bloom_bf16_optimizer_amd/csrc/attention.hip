@@ -319,47 +319,15 @@ __device__ __forceinline__ void attn_state_init(AttnState<D>& st) {
   st.l = 0.f;
 }
 
-// A finished row, normalised, into a staged output tile: the two lane halves
-// hold the sums over complementary keys; lane half h holds
-// d = 32*dt + 8*g + 4*h + 0..3 of row `row` (0..127) of the tile, bf16
-// row-major with 16-byte chunk c of row r at c ^ (r % CPR), so that the
-// writes of 32 rows and the whole-row reads of attn_store_tile are free of
-// bank conflicts.  Also writes the row's lse (natural log) if ok.
+// A finished row, normalised, into the staged output tile (attn_stage_row:
+// the two lane halves hold the sums over complementary keys), and its lse
+// (natural log) if ok.
 template <int D>
 __device__ __forceinline__ void attn_row_to_tile(const AttnState<D>& st, char* otile, int row, float* __restrict__ lse,
                                                  int64_t lrow, bool ok, int half) {
-  constexpr int CPR = D / 8;
   const float l_tot = st.l + __shfl_xor(st.l, 32, kWave);
-  const float inv = 1.0f / l_tot;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint32_t lo = pack2(st.oacc[dt][4 * g] * inv, st.oacc[dt][4 * g + 1] * inv);
-      const uint32_t hi = pack2(st.oacc[dt][4 * g + 2] * inv, st.oacc[dt][4 * g + 3] * inv);
-      const int c = (4 * dt + g) ^ (row % CPR);
-      *reinterpret_cast<uint2*>(otile + row * (2 * D) + 16 * c + 8 * half) = make_uint2(lo, hi);
-    }
+  attn_stage_row<D>(st.oacc, 1.0f / l_tot, otile, 32 * 2 * D, row, half);
   if (ok && half == 0) lse[lrow] = (st.m + __log2f(l_tot)) * 0.69314718055994530942f;
-}
-
-// The staged output tile of 128 rows to o rows row0 .. (rows past `valid`
-// are not stored): NT threads store whole rows, 16 bytes each, instead of
-// each lane storing 8-byte pieces of 16 different rows.
-template <int D, int NT>
-__device__ __forceinline__ void attn_store_tile(const char* otile, uint2* __restrict__ o, int64_t row0, int valid,
-                                                int t) {
-  constexpr int CPR = D / 8;
-  constexpr int PER = kAttnBlockM * CPR / NT;  // 16-byte chunks per thread
-  static_assert(PER >= 1 && kAttnBlockM * CPR % NT == 0, "output tile chunks");
-  uint4* o4 = reinterpret_cast<uint4*>(o);
-#pragma unroll
-  for (int x = 0; x < PER; ++x) {
-    const int chunk = x * NT + t;
-    const int row = chunk / CPR, c = chunk % CPR;
-    const uint4 val = *reinterpret_cast<const uint4*>(otile + row * (2 * D) + 16 * (c ^ (row % CPR)));
-    if (row < valid) o4[(row0 + row) * CPR + c] = val;
-  }
 }
 
 template <int D>
@@ -495,7 +463,8 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
     // refills after its own first barrier).
     __syncthreads();
     if (has_next) request_first(nxt);
-    attn_store_tile<D, kAttnThreads>(otile, o, base + qb * kAttnBlockM, seq - qb * kAttnBlockM, t);
+    attn_store_staged<D, kAttnBlockM, kAttnThreads>(otile, 32 * 2 * D, o, base + qb * kAttnBlockM,
+                                                    seq - qb * kAttnBlockM, t);
     if (!has_next) break;  // uniform over the workgroup
     j = jn;
     cur = nxt;
@@ -567,7 +536,8 @@ __global__ __launch_bounds__(kAttnGroupThreads) __attribute__((amdgpu_waves_per_
   static_assert(sizeof(tiles) >= kAttnBlockM * D * 2, "output tile");
   attn_row_to_tile<D>(st, otile, w * 32 + col, lse, base + qi, qi < seq, half);
   __syncthreads();
-  attn_store_tile<D, kAttnGroupThreads>(otile, o, base + qb * kAttnBlockM, seq - qb * kAttnBlockM, t);
+  attn_store_staged<D, kAttnBlockM, kAttnGroupThreads>(otile, 32 * 2 * D, o, base + qb * kAttnBlockM,
+                                                      seq - qb * kAttnBlockM, t);
 }
 
 bloom_status check_attention(int64_t batch, int32_t heads, int64_t seq, int32_t head_dim) {

@@ -356,10 +356,16 @@ __device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, cons
       for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
     walk(std::integral_constant<bool, false>(), acc, dsum, qvalid ? dl : 0.f, jn,
          has_next ? nkb_of(qblocks - 1 - jn / bh_count) : 1, has_next);
+    // The stage the last block used takes the dq rows (32-row groups QP
+    // bytes apart) for stores of whole rows; with 64-query items the
+    // key-half-1 waves first hand their dQ^T to the key-half-0 waves of the
+    // same queries through the same memory, each tile's rows inside its own
+    // hand-over area.
+    constexpr int QP = QI == 64 ? DT * 16 * kWave * 4 : 32 * 2 * D;
+    static_assert(QP >= 32 * 2 * D && (QI / 32) * QP <= 2 * CH * 16, "dq rows in one stage");
+    char* stage_bytes = reinterpret_cast<char*>(&tiles[buf ^ 1][0][0]);
     if (QI == 64) {
-      // the key-half-1 waves hand their dQ^T to the key-half-0 waves of the
-      // same queries through the stage the last block used
-      float* xch = reinterpret_cast<float*>(&tiles[buf ^ 1][0][0]) + qt * (DT * 16 * kWave);
+      float* xch = reinterpret_cast<float*>(stage_bytes + qt * QP);
       if (kh == 1) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -374,19 +380,11 @@ __device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, cons
           for (int i = 0; i < 16; ++i) acc[dt][i] += xch[(dt * 16 + i) * kWave + lane];
       }
     }
+    if (kh == 0) attn_stage_row<D>(acc, scale, stage_bytes, QP, qt * 32 + col, half);
     // this item's q, dO and lse are no longer needed: the next item's load now
     if (has_next) load_rows(jn);
-    if (writer) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          // d = 32*dt + 8*gg + 4*half + 0..3
-          const uint32_t lo = pack2(acc[dt][4 * gg] * scale, acc[dt][4 * gg + 1] * scale);
-          const uint32_t hi = pack2(acc[dt][4 * gg + 2] * scale, acc[dt][4 * gg + 3] * scale);
-          dq[(base + qi) * (D / 4) + (32 * dt + 8 * gg + 4 * half) / 4] = make_uint2(lo, hi);
-        }
-    }
+    __syncthreads();
+    attn_store_staged<D, QI, kBwdThreads>(stage_bytes, QP, dq, base + qb * QI, seq - qb * QI, t);
     if (!has_next) break;  // uniform over the workgroup
     j = jn;
   }
@@ -723,19 +721,16 @@ __device__ __forceinline__ void dkdv_walk(KvShared<D>& sh, const uint4* __restri
       attn_wait_loads();
       __syncthreads();
     }
+    // dV rows through the stage the last block used, dK rows through the P
+    // exchange, each stored as whole rows by the waves of its role
+    char* rows = DSW ? reinterpret_cast<char*>(&sh.pbuf[0][0][0]) : reinterpret_cast<char*>(&sh.tiles[buf ^ 1][0][0]);
+    static_assert(kBwdBlock * 2 * D <= sizeof(sh.pbuf) && kBwdBlock * 2 * D <= sizeof(sh.tiles[0]), "staged rows");
+    attn_stage_row<D>(acc, outscale, rows, 32 * 2 * D, kgrp * 32 + col, half);
     // this item's key rows are no longer needed: the next item's load now
     if (has_next) load_keys(jn);
-    if (kvalid) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          // d = 32*dt + 8*gg + 4*half + 0..3
-          const int64_t at = (base + kj) * (D / 4) + (32 * dt + 8 * gg + 4 * half) / 4;
-          out[at] = make_uint2(pack2(acc[dt][4 * gg] * outscale, acc[dt][4 * gg + 1] * outscale),
-                               pack2(acc[dt][4 * gg + 2] * outscale, acc[dt][4 * gg + 3] * outscale));
-        }
-    }
+    __syncthreads();
+    attn_store_staged<D, kBwdBlock, 4 * kWave>(rows, 32 * 2 * D, out, base + kb * kBwdBlock, seq - kb * kBwdBlock,
+                                               t & (4 * kWave - 1));
     if (!has_next) break;  // uniform over the workgroup
     j = jn;
   }

@@ -55,6 +55,53 @@ __device__ __forceinline__ void attn_wait_loads() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt not waited for
 }
 
+// Output rows staged through LDS so that they can be stored whole.  A lane
+// holds row `row` of a tile of 32-row groups in 32x32 accumulator fragments
+// (lane half h: d = 32*dt + 8*g + 4*h + 0..3); attn_stage_row writes them,
+// times s, as bf16 into the tile: row r at (r / 32) * GP + (r % 32) * 2D
+// bytes (GP: the bytes between 32-row groups), 16-byte chunk c of a row at
+// c ^ (r % (D/8)), so that 32 rows written at once and whole rows read
+// back are free of bank conflicts.
+template <int D>
+__device__ __forceinline__ void attn_stage_row(const f32x16_t (&acc)[D / 32], float s, char* tile, int gp, int row,
+                                               int half) {
+  constexpr int CPR = D / 8;
+  // the offsets below are cheap to form here; kept opaque so that the
+  // compiler does not hoist them out of the caller's loops into registers
+  asm volatile("" : "+v"(row));
+  char* rp = tile + (row / 32) * gp + (row % 32) * (2 * D);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t lo = pack2(acc[dt][4 * g] * s, acc[dt][4 * g + 1] * s);
+      const uint32_t hi = pack2(acc[dt][4 * g + 2] * s, acc[dt][4 * g + 3] * s);
+      const int c = (4 * dt + g) ^ (row % CPR);
+      *reinterpret_cast<uint2*>(rp + 16 * c + 8 * half) = make_uint2(lo, hi);
+    }
+}
+
+// The ROWS staged rows to rows row0 .. of a [*, D] bf16 matrix: NT threads
+// store 16 bytes each (whole rows, instead of each lane storing 8-byte
+// pieces of 16 rows); rows at or past `valid` are not stored.
+template <int D, int ROWS, int NT>
+__device__ __forceinline__ void attn_store_staged(const char* tile, int gp, uint2* __restrict__ out, int64_t row0,
+                                                  int valid, int t) {
+  constexpr int CPR = D / 8;
+  constexpr int PER = ROWS * CPR / NT;  // 16-byte chunks per thread
+  static_assert(PER >= 1 && ROWS * CPR % NT == 0, "staged rows");
+  uint4* o4 = reinterpret_cast<uint4*>(out);
+  asm volatile("" : "+v"(t));  // as in attn_stage_row
+#pragma unroll
+  for (int x = 0; x < PER; ++x) {
+    const int chunk = x * NT + t;
+    const int row = chunk / CPR, c = chunk % CPR;
+    const uint4 val =
+        *reinterpret_cast<const uint4*>(tile + (row / 32) * gp + (row % 32) * (2 * D) + 16 * (c ^ (row % CPR)));
+    if (row < valid) o4[(row0 + row) * CPR + c] = val;
+  }
+}
+
 // A 64-bit pointer made wave-uniform (both halves through readfirstlane), so
 // that it can sit in the SGPR pair the transfer instruction takes.
 template <typename T>
