@@ -480,7 +480,8 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
 // wins when the longest item is a large share of a unit's work.  Workgroup i
 // takes item i (heaviest first; on XCD i % 8 with xcd_split).
 template <int D>
-__global__ __launch_bounds__(kAttnGroupThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_fwd_stream_kernel(
+__global__ __launch_bounds__(kAttnGroupThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attention_fwd_stream_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
     uint2* __restrict__ o, float* __restrict__ lse, int seq, int heads, int qblocks, int bh_count,
     bool xcd_split, float scale2, AttnSlopes slopes) {

@@ -152,7 +152,8 @@ __device__ __forceinline__ Bf16Split2 split_bf16x2(float a0, float b0, float a1,
 // the row's D = delta and accumulates dQ^T over the half's two 16-key steps
 // right after forming it.
 template <int D, bool DIAG, bool SUM, int NKT>
-__device__ __forceinline__ void dq_block(f32x16_t (&acc)[D / 32], float& dsum, const attn_lds_uint4* __restrict__ kt_lds,
+__device__ __forceinline__ void dq_block(f32x16_t (&acc)[D / 32], float& dsum,
+                                         const attn_lds_uint4* __restrict__ kt_lds,
                                          const attn_lds_uint4* __restrict__ vt_lds, const bf16x8_t (&qf)[D / 16],
                                          const bf16x8_t (&df)[D / 16], float scale2, float slope2, float lse2,
                                          float delta, int k0, int kt0, int qi, int half, int col, int lane) {
@@ -422,7 +423,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 // tile (rows tr0 .. tr0+31 of the staged 64, global queries qt0 ..); p goes
 // to LDS as FP32 and into pf as bf16.
 template <int D, bool MASK>
-__device__ __forceinline__ void p_tile(bf16x8_t (&pf)[2], float4* __restrict__ pout, const attn_lds_uint4* __restrict__ q_lds,
+__device__ __forceinline__ void p_tile(bf16x8_t (&pf)[2], float4* __restrict__ pout,
+                                       const attn_lds_uint4* __restrict__ q_lds,
                                        const float4* lse_lds, const bf16x8_t (&kf)[D / 16], float scale2, float slope2,
                                        int kj, int tr0, int qt0, int seq, int half, int col, int lane) {
   using T = BwdTile<D>;
@@ -754,7 +756,8 @@ size_t bwd_workspace(int64_t batch, int32_t heads, int64_t seq) {
 }
 
 template <int D>
-void launch_bwd(const bloom_bf16* q, const bloom_bf16* k, const bloom_bf16* v, const bloom_bf16* dout, const float* lse, bloom_bf16* dq, bloom_bf16* dk, bloom_bf16* dv,
+void launch_bwd(const bloom_bf16* q, const bloom_bf16* k, const bloom_bf16* v, const bloom_bf16* dout, const float* lse,
+                bloom_bf16* dq, bloom_bf16* dk, bloom_bf16* dv,
                 float* delta, int64_t batch, int32_t heads, int64_t seq, float scale2, float scale,
                 const AttnSlopes& table, hipStream_t stream) {
   const int bh_count = (int)(batch * heads);
