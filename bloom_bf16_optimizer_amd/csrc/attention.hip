@@ -436,10 +436,11 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
         for (int i = 0; i < 16; ++i) mg[(dt * 16 + i) * kWave] = st.oacc[dt][i];
       mg[(DT * 16) * kWave] = st.m;
       mg[(DT * 16 + 1) * kWave] = st.l;
-      // stream 1's next Q arrives during the merge (this item's Q is done)
-      if (has_next) attn_load_q<D>(qf, q, nxt.bh * (int64_t)seq + q_row(nxt), q_row(nxt) < seq, half);
     }
     __syncthreads();
+    // stream 1's next Q arrives during the merge (this item's Q is done)
+    if (stream == 1 && has_next)
+      attn_load_q<D>(qf, q, nxt.bh * (int64_t)seq + q_row(nxt), q_row(nxt) < seq, half);
     if (stream == 0) {
       const float m1 = mg[(DT * 16) * kWave], l1 = mg[(DT * 16 + 1) * kWave];
       const float m = fmaxf(st.m, m1);
