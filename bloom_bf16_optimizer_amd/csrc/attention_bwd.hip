@@ -382,10 +382,10 @@ __device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, cons
       }
     }
     if (kh == 0) attn_stage_row<D>(acc, scale, stage_bytes, QP, qt * 32 + col, half);
-    // this item's q, dO and lse are no longer needed: the next item's load now
-    if (has_next) load_rows(jn);
     __syncthreads();
     attn_store_staged<D, QI, kBwdThreads>(stage_bytes, QP, dq, base + qb * QI, seq - qb * QI, t);
+    // this item's q, dO and lse are no longer needed: the next item's load now
+    if (has_next) load_rows(jn);
     if (!has_next) break;  // uniform over the workgroup
     j = jn;
   }
@@ -728,11 +728,11 @@ __device__ __forceinline__ void dkdv_walk(KvShared<D>& sh, const uint4* __restri
     char* rows = DSW ? reinterpret_cast<char*>(&sh.pbuf[0][0][0]) : reinterpret_cast<char*>(&sh.tiles[buf ^ 1][0][0]);
     static_assert(kBwdBlock * 2 * D <= sizeof(sh.pbuf) && kBwdBlock * 2 * D <= sizeof(sh.tiles[0]), "staged rows");
     attn_stage_row<D>(acc, outscale, rows, 32 * 2 * D, kgrp * 32 + col, half);
-    // this item's key rows are no longer needed: the next item's load now
-    if (has_next) load_keys(jn);
     __syncthreads();
     attn_store_staged<D, kBwdBlock, 4 * kWave>(rows, 32 * 2 * D, out, base + kb * kBwdBlock, seq - kb * kBwdBlock,
                                                t & (4 * kWave - 1));
+    // this item's key rows are no longer needed: the next item's load now
+    if (has_next) load_keys(jn);
     if (!has_next) break;  // uniform over the workgroup
     j = jn;
   }
