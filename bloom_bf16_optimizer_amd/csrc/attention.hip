@@ -269,34 +269,6 @@ __device__ __forceinline__ AttnItem attn_item(int j, int qblocks, int bh_count, 
   return it;
 }
 
-// ALiBi offset fragments: k-slots 0..2 of the lower lane half carry the key
-// offset in the block (an integer < 64, exact in bf16) in kx, against
-// slope/scale split into three bf16 parts in qx; every other slot is zero.
-__device__ __forceinline__ void attn_key_offsets(bf16x8_t (&kx)[2], int half, int col) {
-  const __bf16 z = (__bf16)0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const bool on = half == 0 && j < 3;
-    kx[0][j] = on ? (__bf16)(float)col : z;
-    kx[1][j] = on ? (__bf16)(float)(col + 32) : z;
-  }
-}
-__device__ __forceinline__ bf16x8_t attn_slope_parts(float slope2, float scale2, int half) {
-  const float cs = slope2 / scale2;  // slope/scale
-  const __bf16 c1 = (__bf16)cs;
-  const float r1 = cs - (float)c1;
-  const __bf16 c2 = (__bf16)r1;
-  const __bf16 c3 = (__bf16)(r1 - (float)c2);
-  const __bf16 z = (__bf16)0.0f;
-  bf16x8_t qx;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const bool on = half == 0 && j < 3;
-    qx[j] = on ? (j == 0 ? c1 : (j == 1 ? c2 : c3)) : z;
-  }
-  return qx;
-}
-
 // Q^T operand fragments of a query row: lane supplies q[row][16*kk + 8*half .. +8]
 // (zeros past the sequence).
 template <int D>

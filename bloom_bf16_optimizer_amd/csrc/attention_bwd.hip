@@ -17,7 +17,9 @@
 //    blocks, 64 queries, a wave 32 of them against half the keys), and
 //    streams the key blocks (64 keys, K and V staged in LDS) up to its
 //    diagonal twice.  Both passes form S^T = K Q^T and dP^T = V dO^T so that
-//    lane l owns query l%32 (its lse and D_i are one number each).  The first
+//    lane l owns query l%32 (its lse and D_i are one number each); as in the
+//    forward, the ALiBi offset of a key within its 32-key half enters S^T as
+//    one more MFMA k-step, so a score costs one FMA before exp2.  The first
 //    sums D_i = sum_j p_ij dp_ij in FP32 and writes it to the workspace for
 //    the dk/dv kernel; the second forms dS with that D and dQ^T += K^T dS^T
 //    with K^T read from the same LDS tile by the transposing
@@ -155,7 +157,8 @@ template <int D, bool DIAG, bool SUM, int NKT>
 __device__ __forceinline__ void dq_block(f32x16_t (&acc)[D / 32], float& dsum,
                                          const attn_lds_uint4* __restrict__ kt_lds,
                                          const attn_lds_uint4* __restrict__ vt_lds, const bf16x8_t (&qf)[D / 16],
-                                         const bf16x8_t (&df)[D / 16], float scale2, float slope2, float lse2,
+                                         const bf16x8_t (&df)[D / 16], const bf16x8_t& kx, const bf16x8_t& qx,
+                                         float scale2, float slope2, float lse2,
                                          float delta, int k0, int kt0, int qi, int half, int col, int lane) {
   using T = BwdTile<D>;
   constexpr int KS = D / 16, DT = D / 32;
@@ -163,8 +166,6 @@ __device__ __forceinline__ void dq_block(f32x16_t (&acc)[D / 32], float& dsum,
   const int sw = T::swz(col);  // also the swizzle of row col + 32
   const attn_lds_u32x4* k0r = reinterpret_cast<const attn_lds_u32x4*>(kt_lds) + col * T::CPR;
   const attn_lds_u32x4* v0r = reinterpret_cast<const attn_lds_u32x4*>(vt_lds) + col * T::CPR;
-  // base-2 logit minus lse: s*scale2 + slope2*(key - qi) - lse2
-  const float cb = fmaf(slope2, (float)(k0 + 4 * half - qi), -lse2);
   // transposing reads of K for dQ^T += K^T dS^T
   const int tj = (lane & 15) >> 2, tc = lane & 3, tg = (lane >> 4) & 1;
   const int trow = 4 * half + tj;
@@ -174,10 +175,12 @@ __device__ __forceinline__ void dq_block(f32x16_t (&acc)[D / 32], float& dsum,
 #pragma unroll
   for (int u = 0; u < NKT; ++u) {
     const int kt = kt0 + u;
-    f32x16_t s = zero, dp = zero;
+    f32x16_t dp = zero;
     // the score products at a raised issue priority: the other wave of the
-    // SIMD then fills the gaps of this chain instead of delaying it
+    // SIMD then fills the gaps of this chain instead of delaying it; the
+    // first k-step adds the key's offset in the half times slope/scale
     __builtin_amdgcn_s_setprio(1);
+    f32x16_t s = mfma32(kx, qx, zero);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const int c = 32 * kt * T::CPR + ((2 * kk + half) ^ sw);
@@ -187,10 +190,12 @@ __device__ __forceinline__ void dq_block(f32x16_t (&acc)[D / 32], float& dsum,
     __builtin_amdgcn_s_setprio(0);
     attn_u32x4 dsh[2], dsl[2];  // the bf16x8 operands of each part, as dwords
     float pp[2];
+    // base-2 logit minus lse: s*scale2 + slope2*(k0 + 32*kt - qi) - lse2
+    const float cb = fmaf(slope2, (float)(k0 + 32 * kt - qi), -lse2);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int off = 32 * kt + 8 * (i / 4) + (i % 4);  // key - k0 - 4*half
-      float p = __builtin_amdgcn_exp2f(fmaf(s[i], scale2, fmaf(slope2, (float)off, cb)));
+      float p = __builtin_amdgcn_exp2f(fmaf(s[i], scale2, cb));
       if (DIAG && k0 + 4 * half + off > qi) p = 0.f;
       if (SUM) {
         dsum = fmaf(p, dp[i], dsum);
@@ -263,6 +268,8 @@ __device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, cons
   if (j >= n_items) return;  // uniform over the workgroup
   // B operands: this lane's query row of q and dO (d = 16*kk + 8*half .. +8)
   bf16x8_t qf[KS], df[KS];
+  bf16x8_t kx[2];  // kx[0]: the key offset in a 32-key half (kx[1] unused)
+  attn_key_offsets(kx, half, col);
   float lse2;
   auto load_rows = [&](int jn) {
     const int qb_ = qblocks - 1 - jn / bh_count;
@@ -294,6 +301,7 @@ __device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, cons
     const int64_t bh = j % bh_count;
     const int h = (int)(bh % heads);
     const float slope2 = slopes.s[h];
+    const bf16x8_t qx = attn_slope_parts(slope2, scale2, half);
     const int64_t base = bh * (int64_t)seq;
     const int q0 = qb * QI + qt * 32;  // this wave's first query
     const int qi = q0 + col;
@@ -321,11 +329,11 @@ __device__ __forceinline__ void bwd_query_pass(const uint4* __restrict__ q, cons
           request_block(nj, nkb_next - 1, buf ^ 1);
         if (wave_live && kw0 <= q0 + 31) {
           if (kw0 + 32 * NKT - 1 > q0)
-            dq_block<D, true, SUM, NKT>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2, delta,
-                                        k0, kh, qi, half, col, lane);
+            dq_block<D, true, SUM, NKT>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, kx[0], qx, scale2, slope2,
+                                        lse2, delta, k0, kh, qi, half, col, lane);
           else
-            dq_block<D, false, SUM, NKT>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, scale2, slope2, lse2,
-                                         delta, k0, kh, qi, half, col, lane);
+            dq_block<D, false, SUM, NKT>(acc, dsum, tile(buf, 0), tile(buf, 1), qf, df, kx[0], qx, scale2, slope2,
+                                         lse2, delta, k0, kh, qi, half, col, lane);
         }
         attn_wait_loads();
         __syncthreads();

@@ -24,6 +24,36 @@ __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b,
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
+// ALiBi offset fragments for the score products S^T = K Q^T: k-slots 0..2
+// of the lower lane half carry the key's offset in its block (an integer
+// < 64, exact in bf16) in kx (kx[1]: the block's second 32 keys), against
+// slope/scale split into three bf16 parts in qx; every other slot is zero.
+// One more MFMA k-step with them adds offset * slope/scale to every score.
+__device__ __forceinline__ void attn_key_offsets(bf16x8_t (&kx)[2], int half, int col) {
+  const __bf16 z = (__bf16)0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bool on = half == 0 && j < 3;
+    kx[0][j] = on ? (__bf16)(float)col : z;
+    kx[1][j] = on ? (__bf16)(float)(col + 32) : z;
+  }
+}
+__device__ __forceinline__ bf16x8_t attn_slope_parts(float slope2, float scale2, int half) {
+  const float cs = slope2 / scale2;  // slope/scale
+  const __bf16 c1 = (__bf16)cs;
+  const float r1 = cs - (float)c1;
+  const __bf16 c2 = (__bf16)r1;
+  const __bf16 c3 = (__bf16)(r1 - (float)c2);
+  const __bf16 z = (__bf16)0.0f;
+  bf16x8_t qx;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bool on = half == 0 && j < 3;
+    qx[j] = on ? (j == 0 ? c1 : (j == 1 ? c2 : c3)) : z;
+  }
+  return qx;
+}
+
 typedef __attribute__((address_space(3))) uint4 attn_lds_uint4;
 typedef unsigned int attn_u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) attn_u32x4 attn_lds_u32x4;
